@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the oracle leg.
+
+This module holds workload shapes and random number generation only: none of
+the attention arithmetic.  It imports nothing from ``oracle/`` or from the
+HIP binding, so both sides of a parity check can take their inputs from it.
+
+Recipe.  Every tensor is i.i.d. N(0, 1) drawn in float32 from a
+``torch.Generator`` seeded with ``seed * 16 + tensor_id`` on the device the
+tensor lives on, then rounded to bfloat16 (round-to-nearest-even, torch's
+cast) for the bf16 workloads.  Cache positions past a sequence's valid length
+are filled with NaN, so a kernel that reads padding poisons its output.  The
+softmax scale is the float32 value of ``1/sqrt(d)``.
+
+Workloads follow the Llama3-70B attention geometry of the pages (H_q = 64,
+H_kv = 8, G = 8, d = 128; ADR-0060@5a76ed4 §0 "Reference dimensions") at the
+lengths of the five measured cases below.  No dataset or trained weights are
+involved.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "decode" or "prefill"
+    B: int
+    H_q: int
+    H_kv: int
+    d: int
+    dtype: str           # "f32" or "bf16"
+    lens: tuple = ()     # decode: valid KV length per sequence
+    kv_cap: int = 0      # decode: cache capacity (padded length)
+    S_q: int = 0         # prefill: query chunk length
+    S_kv: int = 0        # prefill: keys in the cache
+    causal: bool = True
+    offset: int = 0      # prefill: cached tokens before the chunk
+
+    @property
+    def G(self) -> int:
+        return self.H_q // self.H_kv
+
+    @property
+    def scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32))
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def max_kv_len(self) -> int:
+        return max(self.lens) if self.kind == "decode" else self.S_kv
+
+    def kv_bytes(self) -> int:
+        """K+V bytes a decode step must read: valid keys only, padding excluded."""
+        return 2 * sum(self.lens) * self.H_kv * self.d * self.elem_bytes
+
+    def decode_bytes(self) -> int:
+        """Algorithmic bytes of one decode call: K+V of the valid keys, Q and O."""
+        qo = 2 * self.B * self.H_q * self.d * self.elem_bytes
+        return self.kv_bytes() + qo
+
+    def visible_pairs_per_head(self) -> int:
+        """(query, key) pairs a causal prefill chunk must score, per head."""
+        if not self.causal:
+            return self.S_q * self.S_kv
+        return sum(self.offset + i + 1 for i in range(self.S_q))
+
+    def prefill_flops(self) -> int:
+        """Algorithmic FLOPs: 2*d for Q.K^T plus 2*d for P.V per visible pair."""
+        return 4 * self.d * self.B * self.H_q * self.visible_pairs_per_head()
+
+
+WORKLOADS = {
+    "decode_small_f32": Workload("decode_small_f32", "decode", B=1, H_q=8, H_kv=1,
+                                 d=128, dtype="f32", lens=(256,), kv_cap=256),
+    "decode_llama70b_32k": Workload("decode_llama70b_32k", "decode", B=1, H_q=64,
+                                    H_kv=8, d=128, dtype="bf16", lens=(32768,),
+                                    kv_cap=32768),
+    "decode_ragged_b4": Workload("decode_ragged_b4", "decode", B=4, H_q=64, H_kv=8,
+                                 d=128, dtype="bf16",
+                                 lens=(8192, 32768, 65536, 131072), kv_cap=131072),
+    "prefill_causal_8k": Workload("prefill_causal_8k", "prefill", B=1, H_q=64,
+                                  H_kv=8, d=128, dtype="bf16", S_q=8192,
+                                  S_kv=8192, causal=True, offset=0),
+    "prefill_chunk_64k": Workload("prefill_chunk_64k", "prefill", B=1, H_q=64,
+                                  H_kv=8, d=128, dtype="bf16", S_q=8192,
+                                  S_kv=65536, causal=True, offset=57344),
+}
+
+# Seed per workload: 20260000 + its position in the list above (1-based).
+SEEDS = {name: 20260000 + i + 1 for i, name in enumerate(WORKLOADS)}
+
+
+def _gen(device, seed: int, tensor_id: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 16 + tensor_id)
+    return g
+
+
+def randn(shape, dtype, device, seed: int, tensor_id: int) -> torch.Tensor:
+    """N(0,1) in float32 from a seeded generator, then cast to ``dtype``."""
+    g = _gen(device, seed, tensor_id)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x.to(dtype)
+
+
+def make_decode(w: Workload, device="cpu", seed=None, nan_pad=True, lens=None):
+    """Decode inputs: q ``[B,H_q,d]``, k/v ``[B,H_kv,kv_cap,d]``, kv_lens int32."""
+    seed = SEEDS.get(w.name, 1) if seed is None else seed
+    lens = tuple(w.lens) if lens is None else tuple(lens)
+    dt = w.torch_dtype
+    q = randn((w.B, w.H_q, w.d), dt, device, seed, 0)
+    k = randn((w.B, w.H_kv, w.kv_cap, w.d), dt, device, seed, 1)
+    v = randn((w.B, w.H_kv, w.kv_cap, w.d), dt, device, seed, 2)
+    if nan_pad:
+        for b, L in enumerate(lens):
+            if L < w.kv_cap:
+                k[b, :, L:].fill_(float("nan"))
+                v[b, :, L:].fill_(float("nan"))
+    kv_lens = torch.tensor(lens, dtype=torch.int32, device=device)
+    return {"q": q, "k": k, "v": v, "kv_lens": kv_lens}
+
+
+def make_prefill(w: Workload, device="cpu", seed=None, nan_pad=True, kv_cap=None):
+    """Prefill inputs: q ``[B,H_q,S_q,d]``, k/v ``[B,H_kv,kv_cap,d]``."""
+    seed = SEEDS.get(w.name, 1) if seed is None else seed
+    cap = w.S_kv if kv_cap is None else kv_cap
+    dt = w.torch_dtype
+    q = randn((w.B, w.H_q, w.S_q, w.d), dt, device, seed, 0)
+    k = randn((w.B, w.H_kv, cap, w.d), dt, device, seed, 1)
+    v = randn((w.B, w.H_kv, cap, w.d), dt, device, seed, 2)
+    if nan_pad and cap > w.S_kv:
+        k[:, :, w.S_kv:].fill_(float("nan"))
+        v[:, :, w.S_kv:].fill_(float("nan"))
+    return {"q": q, "k": k, "v": v}
+
+
+def sample_rows(S_q: int, n: int, seed: int, always=(0, 1, 63, 64, 127, 128)):
+    """Seeded sample of ``n`` distinct query positions in ``[0, S_q)``.
+
+    Always includes the listed tile-edge positions (when in range) and the
+    last row, then fills up uniformly without replacement.
+    """
+    fixed = sorted({r for r in tuple(always) + (S_q - 1,) if 0 <= r < S_q})
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(S_q, generator=g).tolist()
+    out = list(fixed)
+    seen = set(fixed)
+    for r in perm:
+        if len(out) >= n:
+            break
+        if r not in seen:
+            out.append(r)
+            seen.add(r)
+    return sorted(out[:n])

@@ -1,0 +1,237 @@
+"""fp64 reference for grouped-query attention (decode and causal prefill).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+What is computed.  The pages state that the kernel is FlashAttention tiling
+with an online softmax and a fused P.V, FlashDecoding's split-KV with a
+log-sum-exp merge, and Ring Attention's rotated KV blocks folded by the same
+online softmax, and that no new mathematics is introduced (ADR-0060@5a76ed4,
+"Status", the "Algorithm lineage" paragraph).  All three reach plain softmax
+attention exactly (up to rounding order), so the reference result is that
+definition written out: ``attend_rows`` below.
+
+The remaining functions restate the page's algorithm steps in the pages'
+order and notation -- the split partial ``(m, l, O)``, the merge, the final
+normalisation and the per-tile streaming update -- so that tests can check,
+in fp64, that composing them gives the definition for any partition and any
+tile size.
+
+Readings taken where the pages are silent (each listed in the design doc):
+  * query head ``h`` reads KV head ``h // G`` (the G query rows of one KV head
+    are stacked contiguously, ADR-0060@5a76ed4 §0 "CUBE Group" and §0.5.3
+    INPUTS, where Q is ``[G, T_q, d]`` per KV head);
+  * the causal mask is the visibility set ``j <= causal_offset + i`` rather
+    than an additive constant (the pages say "additive causal mask" without a
+    value, ADR-0060@5a76ed4 §3 and §5.4);
+  * ``scale`` is applied to ``q . k`` before masking and the max (§3 there);
+  * the natural-log LSE ``m + ln(l)`` is the exported statistic.
+
+All arithmetic is numpy float64.  Inputs of any float dtype are upcast to
+float64 first; callers pass the bf16-rounded values the GPU sees.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def kv_head_of(h: int, H_q: int, H_kv: int) -> int:
+    """KV head read by query head ``h``: ``h // G`` with ``G = H_q / H_kv``.
+
+    ADR-0060@5a76ed4 §0 "Reference dimensions" (G = H_q / H_kv) and the
+    "CUBE Group" paragraph (the G query heads of one KV head are M-folded,
+    ``[G, T_q, d] -> [G*T_q, d]``).
+    """
+    if H_q % H_kv != 0:
+        raise ValueError("H_q must be a multiple of H_kv")
+    return h // (H_q // H_kv)
+
+
+def attend_rows(q_rows, k, v, scale: float, visible_len):
+    """The definition: ``softmax(scale * q k^T over visible keys) v`` in fp64.
+
+    q_rows: ``[n, d]`` query rows of one query head.
+    k, v:   ``[L, d]`` keys and values of its KV head (row j = position j).
+    visible_len: ``[n]`` ints; row i sees keys ``0 .. visible_len[i]-1``.
+        Every entry must be >= 1 and <= L.
+
+    Returns ``(o [n, d], lse [n])`` with ``lse = max_s + ln(sum exp(s - max_s))``
+    over the visible keys.  Keys beyond a row's visible length are never
+    read into the result, so NaN padding there cannot leak in.
+    """
+    q = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    vl = np.asarray(visible_len, dtype=np.int64).reshape(-1)
+    n, L = q.shape[0], k.shape[0]
+    if vl.shape[0] != n:
+        raise ValueError("visible_len must have one entry per query row")
+    if n and (vl.min() < 1 or vl.max() > L):
+        raise ValueError("visible lengths must lie in [1, L]")
+    o = np.empty((n, v.shape[1]), dtype=np.float64)
+    lse = np.empty(n, dtype=np.float64)
+    for i in range(n):
+        kv_i = k[: vl[i]]
+        s = float(scale) * (kv_i @ q[i])
+        mx = s.max()
+        w = np.exp(s - mx)
+        den = w.sum()
+        o[i] = (w @ v[: vl[i]]) / den
+        lse[i] = mx + np.log(den)
+    return o, lse
+
+
+def decode(q, k_cache, v_cache, kv_lens, scale: float):
+    """Decode attention (T_q = 1): every query attends to all valid keys.
+
+    q: ``[B, H_q, d]``; k_cache, v_cache: ``[B, H_kv, kv_cap, d]``;
+    kv_lens: ``[B]`` valid lengths (keys ``0 .. kv_lens[b]-1``).
+    Decode is unmasked: the one new query attends to all past KV
+    (ADR-0060@5a76ed4 §5.2).  Returns ``(o [B, H_q, d], lse [B, H_q])``.
+    """
+    q = np.asarray(q)
+    B, H_q, d = q.shape
+    H_kv = k_cache.shape[1]
+    lens = np.asarray(kv_lens, dtype=np.int64).reshape(-1)
+    o = np.empty((B, H_q, d), dtype=np.float64)
+    lse = np.empty((B, H_q), dtype=np.float64)
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(H_q):
+            kv = kv_head_of(h, H_q, H_kv)
+            ob, lb = attend_rows(q[b, h][None, :], k_cache[b, kv, :L],
+                                 v_cache[b, kv, :L], scale, [L])
+            o[b, h] = ob[0]
+            lse[b, h] = lb[0]
+    return o, lse
+
+
+def prefill_visible_len(rows, S_kv: int, causal: bool, causal_offset: int):
+    """Visible key count per query row of a prefill chunk.
+
+    With a causal mask, query ``i`` of a chunk appended after
+    ``causal_offset`` cached tokens sees keys ``j <= causal_offset + i``
+    (ADR-0060@5a76ed4 §0.5.3 ``q_block_meta {q_start, T_q}`` and §5.4: tiles
+    wholly after the query block are invisible).  Without it, all ``S_kv``.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    if causal:
+        return causal_offset + rows + 1
+    return np.full(rows.shape, S_kv, dtype=np.int64)
+
+
+def prefill(q, k, v, S_kv: int, scale: float, causal: bool = True,
+            causal_offset: int = 0, rows=None, heads=None):
+    """Prefill attention over a chunk of ``S_q`` queries.
+
+    q: ``[B, H_q, S_q, d]``; k, v: ``[B, H_kv, kv_cap, d]`` (first ``S_kv``
+    positions valid).  ``rows`` selects query positions (default: all) and
+    ``heads`` query heads (default: all), for sampled checks of large cases.
+    Returns ``(o [B, len(heads), len(rows), d], lse [B, len(heads), len(rows)])``.
+    """
+    q = np.asarray(q)
+    B, H_q, S_q, d = q.shape
+    H_kv = k.shape[1]
+    rows = np.arange(S_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    heads = np.arange(H_q) if heads is None else np.asarray(heads, dtype=np.int64)
+    vl = prefill_visible_len(rows, S_kv, causal, causal_offset)
+    o = np.empty((B, len(heads), len(rows), d), dtype=np.float64)
+    lse = np.empty((B, len(heads), len(rows)), dtype=np.float64)
+    top = int(vl.max()) if len(rows) else 0
+    for b in range(B):
+        for hi, h in enumerate(heads):
+            kv = kv_head_of(int(h), H_q, H_kv)
+            kk = np.asarray(k[b, kv, :top], dtype=np.float64)
+            vv = np.asarray(v[b, kv, :top], dtype=np.float64)
+            ob, lb = attend_rows(q[b, h][rows], kk, vv, scale, vl)
+            o[b, hi] = ob
+            lse[b, hi] = lb
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# The pages' algorithm, step by step (fp64).  Used by tests to confirm that
+# split-KV partials merged in any order, and the per-tile streaming update at
+# any tile size, reach the definition above.
+# ---------------------------------------------------------------------------
+
+def partial(q_rows, k, v, scale: float):
+    """Unnormalised split partial ``(m, l, O)`` over one contiguous KV split.
+
+    After its sweep each split holds ``m = max_j s_j``,
+    ``l = sum_j exp(s_j - m)`` and ``O = sum_j exp(s_j - m) v_j``, not yet
+    divided by ``l`` (ADR-0060@5a76ed4 §4 "Reduction"; ADR-001@1897945
+    §0.5.4, the intermediate partial table).  ``k``/``v`` hold the split's
+    keys; an empty split returns the identity ``(-inf, 0, 0)``.
+    """
+    q = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, d = q.shape[0], v.shape[1]
+    if k.shape[0] == 0:
+        return (np.full(n, -np.inf), np.zeros(n), np.zeros((n, d)))
+    s = float(scale) * (q @ k.T)
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    return m, p.sum(axis=1), p @ v
+
+
+def merge(a, b):
+    """Log-sum-exp merge of two partials (ADR-0060@5a76ed4 §4 ``merge``).
+
+    ``m = max(m_a, m_b)``; each side is weighted by ``exp(m_side - m)``;
+    ``l`` and ``O`` are the weighted sums.  A side with ``m = -inf`` (an
+    empty split) gets weight 0, so ``(-inf, 0, 0)`` is the identity.
+    """
+    m_a, l_a, o_a = a
+    m_b, l_b, o_b = b
+    m = np.maximum(m_a, m_b)
+    with np.errstate(invalid="ignore"):
+        sa = np.where(np.isneginf(m_a), 0.0, np.exp(m_a - m))
+        sb = np.where(np.isneginf(m_b), 0.0, np.exp(m_b - m))
+    return m, l_a * sa + l_b * sb, o_a * sa[:, None] + o_b * sb[:, None]
+
+
+def finalize(t):
+    """Normalise once at the end: ``O / l`` and ``lse = m + ln(l)``
+    (ADR-0060@5a76ed4 §4, "normalise once" after the merge)."""
+    m, l, o = t
+    return o / l[:, None], m + np.log(l)
+
+
+def online_sweep(q_rows, k, v, scale: float, tile: int, visible_len=None):
+    """The per-tile streaming update over tiles of ``tile`` keys.
+
+    Running state starts at ``(m, l, O) = (-inf, 0, 0)``.  For each tile:
+    ``S = scale * q K_j^T`` (masked entries removed), ``m_new = max(m,
+    rowmax S)``, ``P = exp(S - m_new)``, ``corr = exp(m - m_new)``,
+    ``l = l*corr + rowsum P``, ``O = O*corr + P V_j``, ``m = m_new``
+    (ADR-0060@5a76ed4 §3 "Per-tile op sequence").  A tile holding no visible
+    key for a row leaves that row untouched, as a wholly-future tile is
+    skipped (§5.4 there).  Returns the normalised ``(o, lse)``.
+    """
+    q = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, L, d = q.shape[0], k.shape[0], v.shape[1]
+    vl = (np.full(n, L) if visible_len is None
+          else np.asarray(visible_len, dtype=np.int64).reshape(-1))
+    m = np.full(n, -np.inf)
+    l = np.zeros(n)
+    o = np.zeros((n, d))
+    for j0 in range(0, L, tile):
+        j1 = min(j0 + tile, L)
+        s = float(scale) * (q @ k[j0:j1].T)
+        vis = np.arange(j0, j1)[None, :] < vl[:, None]
+        s = np.where(vis, s, -np.inf)
+        live = vis.any(axis=1)
+        m_new = np.where(live, np.maximum(m, s.max(axis=1)), m)
+        with np.errstate(invalid="ignore"):
+            p = np.where(vis, np.exp(s - m_new[:, None]), 0.0)
+            # exp(-inf - finite) = 0 discards the empty initial state.
+            corr = np.where(live, np.exp(m - m_new), 1.0)
+        l = l * corr + p.sum(axis=1)
+        o = o * corr[:, None] + p @ v[j0:j1]
+        m = m_new
+    return o / l[:, None], m + np.log(l)

@@ -1,0 +1,55 @@
+"""Plant plausible mistakes in a copy of the oracle and check a pin catches each.
+
+Each mutant is the oracle's source with one textual change (a dropped term, a
+wrong sign, a wrong index or operand), executed as a fresh module on the CPU.
+The pins must reject every mutant: otherwise they would not pin the oracle.
+"""
+
+import os
+import types
+
+import pytest
+
+import oracle_pins
+
+SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "oracle", "attention.py")
+
+MUTANTS = {
+    "head_map_modulo": ("return h // (H_q // H_kv)", "return h % H_kv"),
+    "dropped_scale": ("s = float(scale) * (kv_i @ q[i])", "s = (kv_i @ q[i])"),
+    "causal_off_by_one": ("return causal_offset + rows + 1", "return causal_offset + rows + 2"),
+    "max_sign": ("w = np.exp(s - mx)", "w = np.exp(s + mx)"),
+    "lse_dropped_max": ("lse[i] = mx + np.log(den)", "lse[i] = np.log(den)"),
+    "values_from_keys": ("o[i] = (w @ v[: vl[i]]) / den", "o[i] = (w @ k[: vl[i]]) / den"),
+    "merge_weight_sign": ("sa = np.where(np.isneginf(m_a), 0.0, np.exp(m_a - m))",
+                          "sa = np.where(np.isneginf(m_a), 0.0, np.exp(m - m_a))"),
+    "sweep_no_rescale": ("o = o * corr[:, None] + p @ v[j0:j1]", "o = o + p @ v[j0:j1]"),
+    "partial_unshifted": ("p = np.exp(s - m[:, None])", "p = np.exp(s)"),
+    "decode_drops_last_key": ("k_cache[b, kv, :L],\n", "k_cache[b, kv, :L - 1],\n"),
+    "keys_reversed": ("s = float(scale) * (q @ k.T)", "s = float(scale) * (q @ k[::-1].T)"),
+    "visible_ignored": ("vis = np.arange(j0, j1)[None, :] < vl[:, None]",
+                        "vis = np.arange(j0, j1)[None, :] < L + 0 * vl[:, None]"),
+}
+
+
+def _load_mutant(old, new):
+    src = open(SRC_PATH).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name):
+    if oracle_pins.mpmath is None:
+        pytest.skip("mpmath not importable")
+    mutant = _load_mutant(*MUTANTS[name])
+    caught = []
+    for pin in oracle_pins.PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, ValueError, IndexError, FloatingPointError) as e:
+            caught.append(f"{pin.__name__}: {type(e).__name__}")
+    assert caught, f"no pin rejects mutant {name}"
