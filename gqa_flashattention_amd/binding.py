@@ -1,0 +1,164 @@
+"""Thin ctypes binding over ``libgqa_attn.so``.
+
+Argument marshalling only: torch tensors supply device pointers, shapes and
+the current HIP stream; every step of the computation runs in the library's
+HIP kernels.  There is no CPU or PyTorch fallback: if the library is missing
+or a call fails, an exception says so.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgqa_attn.so")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
+                3: "GQA_ERR_WORKSPACE", 4: "GQA_ERR_HIP"}
+
+# Every symbol include/gqa_attn.h declares, with its ctypes signature.
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "gqa_attn_status_string": (ctypes.c_char_p, [_i]),
+    "gqa_attn_version": (_i, []),
+    "gqa_attn_decode_split_tokens": (_i, [_i, _i, _i, _i, _i]),
+    "gqa_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "gqa_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
+                             _i, _vp, _sz, _vp]),
+    "gqa_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
+                              _f, _i, _vp]),
+}
+
+
+class GQAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} "
+                         f"({lib().gqa_attn_status_string(status).decode()})")
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m gqa_flashattention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise GQAError(status, where)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("gqa_flashattention_amd runs on the GPU only: got a CPU tensor")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def decode_split_tokens(B, H_kv, max_kv_len, chunk_tokens=0, dtype=DTYPE_BF16) -> int:
+    r = lib().gqa_attn_decode_split_tokens(B, H_kv, max_kv_len, chunk_tokens, dtype)
+    if r < 0:
+        raise GQAError(-r, "gqa_attn_decode_split_tokens")
+    return r
+
+
+def decode_workspace_bytes(B, H_q, H_kv, d, max_kv_len, chunk_tokens=0, dtype=DTYPE_BF16) -> int:
+    n = lib().gqa_attn_decode_workspace_bytes(B, H_q, H_kv, d, max_kv_len, chunk_tokens, dtype)
+    if n == 0:
+        raise GQAError(1, "gqa_attn_decode_workspace_bytes")
+    return n
+
+
+def decode(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chunk_tokens=0,
+           return_lse=False, out=None, lse=None, workspace=None, stream=None):
+    """``gqa_attn_decode`` on torch tensors.
+
+    q ``[B,H_q,d]``, k_cache/v_cache ``[B,H_kv,kv_cap,d]`` (same dtype, bf16 or
+    fp32), kv_lens ``[B]`` int32 on the device.  ``max_kv_len`` defaults to
+    ``kv_cap``.  Returns ``o`` (and ``lse`` when ``return_lse``).
+    """
+    _require_gpu(q, k_cache, v_cache, kv_lens)
+    B, H_q, d = q.shape
+    _, H_kv, kv_cap, _ = k_cache.shape
+    if kv_lens.dtype != torch.int32:
+        raise TypeError("kv_lens must be int32")
+    max_kv_len = kv_cap if max_kv_len is None else int(max_kv_len)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H_q, H_kv, d, max_kv_len, chunk_tokens, dt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().gqa_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens), _ptr(out),
+                               _ptr(lse) if return_lse else None, B, H_q, H_kv, d, kv_cap,
+                               max_kv_len, scale, dt, chunk_tokens, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gqa_attn_decode")
+    return (out, lse) if return_lse else out
+
+
+def prefill(q, k, v, S_kv=None, causal=True, causal_offset=0, scale=None, return_lse=False,
+            out=None, lse=None, stream=None):
+    """``gqa_attn_prefill`` on torch tensors.
+
+    q ``[B,H_q,S_q,d]``, k/v ``[B,H_kv,kv_cap,d]`` bf16.  ``S_kv`` defaults to
+    ``kv_cap``.  Returns ``o`` (and ``lse`` when ``return_lse``).
+    """
+    _require_gpu(q, k, v)
+    B, H_q, S_q, d = q.shape
+    _, H_kv, kv_cap, _ = k.shape
+    S_kv = kv_cap if S_kv is None else int(S_kv)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q, S_q), dtype=torch.float32, device=q.device)
+    st = lib().gqa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                _ptr(lse) if return_lse else None, B, H_q, H_kv, d, S_q, S_kv,
+                                kv_cap, int(bool(causal)), int(causal_offset), scale, dt,
+                                _stream(stream))
+    _check(st, "gqa_attn_prefill")
+    return (out, lse) if return_lse else out

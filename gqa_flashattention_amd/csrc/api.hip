@@ -1,0 +1,172 @@
+// C-ABI entry points: host-side argument validation, work decomposition and
+// kernel launches.  Declarations and the full contract are in
+// include/gqa_attn.h.  Nothing here allocates, frees or synchronises.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "gqa_attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kMaxG = 16;          // query heads per KV head the decode MFMA tile holds
+constexpr int kF32Chunk = 256;     // keys per split of the fp32 decode path
+constexpr int kBf16ChunkQuantum = 128;  // 4 waves x 32-key blocks
+constexpr int kTargetSplits = 1024;     // ~4 workgroups per CU on 256 CUs
+constexpr size_t kWsAlign = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Effective keys per decode split, or a negative status.
+int split_tokens(int B, int H_kv, int max_kv_len, int chunk_tokens, int dtype) {
+  if (B < 1 || H_kv < 1 || max_kv_len < 1 || chunk_tokens < 0) return -GQA_ERR_INVALID_ARG;
+  if (dtype == GQA_DTYPE_F32) {
+    if (chunk_tokens != 0 && chunk_tokens != kF32Chunk) return -GQA_ERR_INVALID_ARG;
+    return kF32Chunk;
+  }
+  if (dtype != GQA_DTYPE_BF16) return -GQA_ERR_INVALID_ARG;
+  if (chunk_tokens > 0) {
+    if (chunk_tokens % kBf16ChunkQuantum != 0) return -GQA_ERR_INVALID_ARG;
+    return chunk_tokens;
+  }
+  const long long rows = (long long)B * H_kv * max_kv_len;
+  long long c = (rows + kTargetSplits - 1) / kTargetSplits;
+  c = (c + kBf16ChunkQuantum - 1) / kBf16ChunkQuantum * kBf16ChunkQuantum;
+  const long long cap = ((long long)max_kv_len + kBf16ChunkQuantum - 1) / kBf16ChunkQuantum * kBf16ChunkQuantum;
+  if (c > cap) c = cap;
+  if (c > 16384) c = 16384;
+  if (c < kBf16ChunkQuantum) c = kBf16ChunkQuantum;
+  return (int)c;
+}
+
+struct WsLayout {
+  size_t o_bytes, ml_off, total;
+};
+
+WsLayout ws_layout(int B, int H_q, int n_split) {
+  WsLayout w;
+  w.o_bytes = (size_t)B * H_q * n_split * kD * sizeof(float);
+  w.ml_off = round_up(w.o_bytes, kWsAlign);
+  w.total = w.ml_off + round_up((size_t)B * H_q * n_split * 2 * sizeof(float), kWsAlign);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_attn_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GQA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GQA_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int gqa_attn_version(void) { return 100; }
+
+int gqa_attn_decode_split_tokens(int B, int H_kv, int max_kv_len, int chunk_tokens, int dtype) {
+  return split_tokens(B, H_kv, max_kv_len, chunk_tokens, dtype);
+}
+
+size_t gqa_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int d, int max_kv_len,
+                                       int chunk_tokens, int dtype) {
+  if (H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || d != kD) return 0;
+  const int chunk = split_tokens(B, H_kv, max_kv_len, chunk_tokens, dtype);
+  if (chunk <= 0) return 0;
+  const int n_split = (max_kv_len + chunk - 1) / chunk;
+  return ws_layout(B, H_q, n_split).total;
+}
+
+int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
+                    int d, int kv_cap, int max_kv_len, float scale, int dtype, int chunk_tokens,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !kv_lens || !o) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return GQA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(kv_lens) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return GQA_ERR_INVALID_ARG;
+  if (B < 1 || H_q < 1 || H_kv < 1 || d < 1 || kv_cap < 1 || max_kv_len < 1)
+    return GQA_ERR_INVALID_ARG;
+  if (H_q % H_kv != 0 || max_kv_len > kv_cap) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16) return GQA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (chunk_tokens < 0) return GQA_ERR_INVALID_ARG;
+  if (B > 65535 || H_kv > 65535) return GQA_ERR_INVALID_ARG;
+  if (d != kD || H_q / H_kv > kMaxG) return GQA_ERR_UNSUPPORTED;
+  const int chunk = split_tokens(B, H_kv, max_kv_len, chunk_tokens, dtype);
+  if (chunk <= 0) return GQA_ERR_INVALID_ARG;
+  const int n_split = (max_kv_len + chunk - 1) / chunk;
+  const WsLayout wl = ws_layout(B, H_q, n_split);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u)) return GQA_ERR_WORKSPACE;
+  if (workspace_bytes < wl.total) return GQA_ERR_WORKSPACE;
+
+  gqa::DecodeParams p;
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.kv_lens = kv_lens;
+  p.o = o;
+  p.lse = lse;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+  p.B = B;
+  p.H_q = H_q;
+  p.H_kv = H_kv;
+  p.G = H_q / H_kv;
+  p.kv_cap = kv_cap;
+  p.chunk = chunk;
+  p.n_split_max = n_split;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = gqa::launch_decode(p, dtype == GQA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H_q, int H_kv, int d, int S_q, int S_kv, int kv_cap, int causal,
+                     int causal_offset, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GQA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return GQA_ERR_INVALID_ARG;
+  if (B < 1 || H_q < 1 || H_kv < 1 || d < 1 || S_q < 1 || S_kv < 1 || kv_cap < 1)
+    return GQA_ERR_INVALID_ARG;
+  if (H_q % H_kv != 0 || S_kv > kv_cap) return GQA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return GQA_ERR_INVALID_ARG;
+  if (causal && (causal_offset < 0 || (long long)causal_offset + S_q > S_kv))
+    return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16) return GQA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (d != kD || dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  const long long n_qblk = ((long long)S_q + gqa::kPrefillBlockM - 1) / gqa::kPrefillBlockM;
+  if (n_qblk * B * H_q > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
+
+  gqa::PrefillParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H_q = H_q;
+  p.H_kv = H_kv;
+  p.G = H_q / H_kv;
+  p.S_q = S_q;
+  p.S_kv = S_kv;
+  p.kv_cap = kv_cap;
+  p.causal = causal;
+  p.offset = causal ? causal_offset : 0;
+  p.n_qblk = (int)n_qblk;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = gqa::launch_prefill(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,379 @@
+// Decode attention (T_q = 1) for gfx950: split-KV partial kernels and the
+// log-sum-exp combine.
+//
+// Method: ADR-0060 "AHBM GQA Fused Attention Kernel (Llama3-70B)", revision
+// 5a76ed4 -- §5.2 (the G query heads of one KV head are folded into the GEMM
+// M dimension so each K/V tile is streamed once for all of them), §3 (the
+// per-tile online-softmax update), §4 (splits produce unnormalised
+// (m, l, O) partials merged by the associative log-sum-exp merge, with one
+// normalisation at the end) and §2.1 (contiguous position blocks per split).
+//
+// GPU mapping.  One workgroup = 4 waves = one contiguous split of
+// `chunk` keys of one (sequence, KV head); wave w sweeps the w-th quarter of
+// the split in blocks of 32 keys, straight from HBM into registers (K and V
+// are read exactly once, so they bypass LDS).  Scores are computed
+// transposed, S^T = K . Q^T, on the 16x16x32 bf16 MFMA with keys in M and
+// the (zero-padded) G <= 16 query heads in N; O^T = V^T . P^T uses the same
+// MFMA with d in M.  The 8x8 transpose V needs is done in registers by byte
+// permutes.  Scores live in the log2 domain (scale * log2(e) folded into one
+// multiply) so the exponentials are single v_exp_f32 instructions.  The 4
+// waves merge through LDS and the workgroup writes one partial.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gqa {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kWaves = 4;
+constexpr int kBlk = 32;  // keys per wave step
+
+// Loads of one 32-key block for one lane.
+//   kreg[sb][kb]: K row (key0 + 16*sb + l%16), d range 32*kb + 8*(l/16) .. +8
+//                 -> A operand of S^T tile sb, k-step kb.
+//   vreg[j]:      V row key(g, j), d range 8*(l%16) .. +8, where
+//                 key(g, j) = 4g + j (j < 4) or 16 + 4g + (j - 4) (j >= 4):
+//                 the keys this lane's P^T slots hold.
+struct Block {
+  u32x4 k[2][4];
+  u32x4 v[8];
+};
+
+template <bool kGuard>
+__device__ __forceinline__ void load_block(Block& blk, const __bf16* kbase, const __bf16* vbase,
+                                           int key0, int kend, int lane) {
+  const int r = lane & 15;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int key = key0 + 16 * sb + r;
+    const bool ok = !kGuard || key < kend;
+    const __bf16* row = kbase + (size_t)key * kD + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      blk.k[sb][kb] = ok ? ld16_stream(row + 32 * kb) : u32x4{0, 0, 0, 0};
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int key = key0 + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
+    const bool ok = !kGuard || key < kend;
+    blk.v[j] = ok ? ld16_stream(vbase + (size_t)key * kD + 8 * r) : u32x4{0, 0, 0, 0};
+  }
+}
+
+// Running state of one wave: query n = lane % 16 (rows >= G are padding).
+struct State {
+  float m;       // running max of log2-domain scores (same on the 4 lanes of n)
+  float l;       // this lane's share of the running sum of p
+  f32x4 o[8];    // O^T, d-tile dt: lane holds d = 8*(4*(lane/16)+i) + dt, query n
+};
+
+template <bool kGuard>
+__device__ __forceinline__ void fold_block(State& st, const Block& blk, const bf16x8 (&qb)[4],
+                                           int key0, int kend, float scale_log2, int lane) {
+  const int g = lane >> 4;
+  // S^T = K . Q^T for two 16-key sub-blocks.
+  f32x4 s[2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(blk.k[sb][kb]), qb[kb], s[sb], 0, 0, 0);
+  }
+  // Scale into the log2 domain; mask keys past the end (guarded block only).
+  float bmax = kNegInf;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = s[sb][i] * scale_log2;
+      if (kGuard && key0 + 16 * sb + 4 * g + i >= kend) x = kNegInf;
+      s[sb][i] = x;
+      bmax = fmaxf(bmax, x);
+    }
+  }
+  bmax = wave_max_xor(bmax, 16);
+  bmax = wave_max_xor(bmax, 32);
+  const float m_new = fmaxf(st.m, bmax);
+  const float corr = fast_exp2(st.m - m_new);  // 0 on the first block (m = -inf)
+  float psum = 0.f;
+  float p[2][4];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[sb][i] = fast_exp2(s[sb][i] - m_new);
+      psum += p[sb][i];
+    }
+  st.l = st.l * corr + psum;
+  st.m = m_new;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] *= corr;
+  // P^T operand: slots 0..3 = sub-block 0 keys 4g+i, slots 4..7 = sub-block 1.
+  u32x4 pw = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+              pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+  const bf16x8 pb = as_bf16x8(pw);
+  // V^T operand for d-tile dt: element j = V[key(g, j)][8*(lane%16) + dt].
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const int w = dt >> 1;
+    u32x4 a;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const unsigned int lo = blk.v[2 * jj][w];
+      const unsigned int hi = blk.v[2 * jj + 1][w];
+      a[jj] = (dt & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pb, st.o[dt], 0, 0, 0);
+  }
+}
+
+}  // namespace
+
+// Grid: (n_split_max, H_kv, B); block: 256 threads.
+__global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParams p) {
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int L = p.kv_lens[b];
+  const int start = split * p.chunk;
+  if (start >= L) return;
+  const int end = min(start + p.chunk, L);
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int quarter = p.chunk / kWaves;
+  const int ws = start + wave * quarter;
+  const int we = min(ws + quarter, end);
+
+  const __bf16* q = static_cast<const __bf16*>(p.q);
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
+
+  // Q^T operand: query n = lane%16 of this KV head's group, zero past G.
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  bf16x8 qb[4];
+  {
+    const bool ok = n < p.G;
+    const __bf16* qrow = q + ((size_t)b * p.H_q + (size_t)kvh * p.G + (ok ? n : 0)) * kD + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) qb[kb] = as_bf16x8(ok ? ld16(qrow + 32 * kb) : u32x4{0, 0, 0, 0});
+  }
+
+  State st;
+  st.m = kNegInf;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (ws < we) {
+    // Two register buffers, A and B, alternate so that the next block's
+    // loads are in flight while the current block is folded.  Only the
+    // last block of the sequence can be partial (guarded).
+    const int nblk = (we - ws + kBlk - 1) / kBlk;
+    const bool tail = (we - ws) % kBlk != 0;
+    Block A, B;
+    auto load_i = [&](Block& bl, int i) {
+      if (tail && i == nblk - 1) load_block<true>(bl, kbase, vbase, ws + i * kBlk, we, lane);
+      else load_block<false>(bl, kbase, vbase, ws + i * kBlk, we, lane);
+    };
+    auto fold_i = [&](const Block& bl, int i) {
+      if (tail && i == nblk - 1) fold_block<true>(st, bl, qb, ws + i * kBlk, we, p.scale_log2, lane);
+      else fold_block<false>(st, bl, qb, ws + i * kBlk, we, p.scale_log2, lane);
+    };
+    load_i(A, 0);
+    for (int i = 0; i < nblk; i += 2) {
+      if (i + 1 < nblk) load_i(B, i + 1);
+      fold_i(A, i);
+      if (i + 1 >= nblk) break;
+      if (i + 2 < nblk) load_i(A, i + 2);
+      fold_i(B, i + 1);
+    }
+  }
+
+  // Per-query sum over the 4 lane groups that share query n.
+  float lsum = wave_sum_xor(st.l, 16);
+  lsum = wave_sum_xor(lsum, 32);
+
+  // Merge the 4 waves through LDS.
+  __shared__ float sm_m[kWaves][16];
+  __shared__ float sm_l[kWaves][16];
+  __shared__ float sm_o[kWaves][16][kD + 4];
+  if (g == 0) {
+    sm_m[wave][n] = st.m;
+    sm_l[wave][n] = lsum;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int dbase = 8 * (4 * g + i);
+    f32x4 lo = {st.o[0][i], st.o[1][i], st.o[2][i], st.o[3][i]};
+    f32x4 hi = {st.o[4][i], st.o[5][i], st.o[6][i], st.o[7][i]};
+    *reinterpret_cast<f32x4*>(&sm_o[wave][n][dbase]) = lo;
+    *reinterpret_cast<f32x4*>(&sm_o[wave][n][dbase + 4]) = hi;
+  }
+  __syncthreads();
+
+  const size_t part0 = ((size_t)b * p.H_q + (size_t)kvh * p.G) * p.n_split_max + split;
+  for (int e = threadIdx.x; e < p.G * kD; e += blockDim.x) {
+    const int qn = e >> 7;
+    const int dd = e & (kD - 1);
+    float mw[kWaves];
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = sm_m[w][qn];
+      M = fmaxf(M, mw[w]);
+    }
+    float acc = 0.f, lacc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = (mw[w] == kNegInf) ? 0.f : fast_exp2(mw[w] - M);
+      acc += wt * sm_o[w][qn][dd];
+      lacc += wt * sm_l[w][qn];
+    }
+    const size_t part = part0 + (size_t)qn * p.n_split_max;
+    p.ws_o[part * kD + dd] = acc;
+    if (dd == 0) {
+      p.ws_ml[2 * part] = M;
+      p.ws_ml[2 * part + 1] = lacc;
+    }
+  }
+}
+
+// fp32 decode partial: one workgroup of 256 threads per 256-key split.  A
+// one-shot partial over the split (score -> max/sum -> P.V, the "fits in
+// scratch" shape of §5.2), all in fp32 on the vector ALUs.
+__global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p) {
+  constexpr int kChunk = 256;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int L = p.kv_lens[b];
+  const int start = split * kChunk;
+  if (start >= L) return;
+  const int cnt = min(kChunk, L - start);
+  const int t = threadIdx.x;
+  const float* q = static_cast<const float*>(p.q) + ((size_t)b * p.H_q + (size_t)kvh * p.G) * kD;
+  const float* kbase = static_cast<const float*>(p.k) + (((size_t)b * p.H_kv + kvh) * p.kv_cap + start) * kD;
+  const float* vbase = static_cast<const float*>(p.v) + (((size_t)b * p.H_kv + kvh) * p.kv_cap + start) * kD;
+
+  __shared__ float sq[16][kD];
+  __shared__ float ss[16][kChunk];
+  __shared__ float sm[16], sl[16];
+  for (int e = t; e < p.G * kD; e += 256) sq[e >> 7][e & (kD - 1)] = q[e];
+  __syncthreads();
+
+  // Scores: thread t owns key start + t.
+  if (t < cnt) {
+    float acc[16];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) acc[n] = 0.f;
+    const float* krow = kbase + (size_t)t * kD;
+    for (int d4 = 0; d4 < kD; d4 += 4) {
+      const f32x4 kv4 = *reinterpret_cast<const f32x4*>(krow + d4);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        if (n < p.G)
+          acc[n] += sq[n][d4] * kv4[0] + sq[n][d4 + 1] * kv4[1] + sq[n][d4 + 2] * kv4[2] + sq[n][d4 + 3] * kv4[3];
+      }
+    }
+    for (int n = 0; n < p.G; ++n) ss[n][t] = acc[n] * p.scale_log2;
+  } else {
+    for (int n = 0; n < p.G; ++n) ss[n][t] = kNegInf;
+  }
+  __syncthreads();
+
+  // Row max and sum: wave w handles queries w, w+4, ...
+  const int wave = t >> 6, lane = t & 63;
+  for (int n = wave; n < p.G; n += 4) {
+    float mx = kNegInf;
+    for (int j = lane; j < kChunk; j += 64) mx = fmaxf(mx, ss[n][j]);
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    float sum = 0.f;
+    for (int j = lane; j < kChunk; j += 64) {
+      const float e = fast_exp2(ss[n][j] - mx);
+      ss[n][j] = e;
+      sum += e;
+    }
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (lane == 0) {
+      sm[n] = mx;
+      sl[n] = sum;
+    }
+  }
+  __syncthreads();
+
+  // O = P . V: thread t -> column d = t % 128, queries t/128, t/128 + 2, ...
+  const int dd = t & (kD - 1);
+  const size_t part0 = ((size_t)b * p.H_q + (size_t)kvh * p.G) * p.n_split_max + split;
+  for (int n = t >> 7; n < p.G; n += 2) {
+    float acc = 0.f;
+    for (int j = 0; j < cnt; ++j) acc += ss[n][j] * vbase[(size_t)j * kD + dd];
+    const size_t part = part0 + (size_t)n * p.n_split_max;
+    p.ws_o[part * kD + dd] = acc;
+    if (dd == 0) {
+      p.ws_ml[2 * part] = sm[n];
+      p.ws_ml[2 * part + 1] = sl[n];
+    }
+  }
+}
+
+// Combine: one workgroup of 128 threads per (sequence, query head); thread
+// t owns output column d = t.  Merges the n_split(b) partials, normalises
+// once and rounds to the output dtype.
+template <typename OutT>
+__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
+  const int bh = blockIdx.x;
+  const int b = bh / p.H_q;
+  const int t = threadIdx.x;
+  const int L = p.kv_lens[b];
+  const int ns = (L + p.chunk - 1) / p.chunk;
+  const size_t part0 = (size_t)bh * p.n_split_max;
+  const float* ml = p.ws_ml + 2 * part0;
+  const float* po = p.ws_o + part0 * kD + t;
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+  float acc = 0.f, lacc = 0.f;
+  int s = 0;
+  for (; s + 4 <= ns; s += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = fast_exp2(ml[2 * (s + u)] - M);
+      acc += w * po[(size_t)(s + u) * kD];
+      lacc += w * ml[2 * (s + u) + 1];
+    }
+  }
+  for (; s < ns; ++s) {
+    const float w = fast_exp2(ml[2 * s] - M);
+    acc += w * po[(size_t)s * kD];
+    lacc += w * ml[2 * s + 1];
+  }
+  const float val = acc / lacc;
+  OutT* o = static_cast<OutT*>(p.o) + (size_t)bh * kD;
+  o[t] = (OutT)val;
+  if (p.lse != nullptr && t == 0) p.lse[bh] = (M + __log2f(lacc)) * kLn2;
+}
+
+hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream) {
+  dim3 grid(p.n_split_max, p.H_kv, p.B);
+  if (bf16) {
+    hipLaunchKernelGGL(decode_partial_bf16_kernel, grid, dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(decode_partial_f32_kernel, grid, dim3(256), 0, stream, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 cgrid(p.B * p.H_q);
+  if (bf16) {
+    hipLaunchKernelGGL(decode_combine_kernel<__bf16>, cgrid, dim3(128), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(decode_combine_kernel<float>, cgrid, dim3(128), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,43 @@
+// Kernel parameter blocks and launchers shared between the HIP kernels and
+// the C-ABI host code.  Plain structs passed by value as kernel arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+struct DecodeParams {
+  const void* q;        // [B, H_q, d]
+  const void* k;        // [B, H_kv, kv_cap, d]
+  const void* v;        // [B, H_kv, kv_cap, d]
+  const int32_t* kv_lens;  // [B] device
+  void* o;              // [B, H_q, d]
+  float* lse;           // [B, H_q] or null
+  float* ws_o;          // [B, H_q, n_split_max, d] unnormalised partial O
+  float* ws_ml;         // [B, H_q, n_split_max, 2] partial (m in log2 units, l)
+  int B, H_q, H_kv, G, kv_cap;
+  int chunk;            // keys per split
+  int n_split_max;      // ceil(max_kv_len / chunk)
+  float scale_log2;     // scale * log2(e)
+};
+
+struct PrefillParams {
+  const void* q;        // [B, H_q, S_q, d]
+  const void* k;        // [B, H_kv, kv_cap, d]
+  const void* v;        // [B, H_kv, kv_cap, d]
+  void* o;              // [B, H_q, S_q, d]
+  float* lse;           // [B, H_q, S_q] or null
+  int B, H_q, H_kv, G, S_q, S_kv, kv_cap;
+  int causal, offset;
+  int n_qblk;           // ceil(S_q / block rows)
+  float scale_log2;
+};
+
+hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+// Rows of queries one prefill workgroup covers.
+constexpr int kPrefillBlockM = 128;
+
+}  // namespace gqa

@@ -1,0 +1,160 @@
+/*
+ * gqa_attn.h -- C ABI of the MI355X (gfx950) grouped-query attention library.
+ *
+ * Two operations, both exact softmax attention computed FlashAttention-style
+ * (tiles of keys folded into a running (m, l, O) state by an online softmax,
+ * P.V fused, no score matrix ever written to memory):
+ *
+ *   gqa_attn_decode   one new query token per sequence (T_q = 1) against a
+ *                     read-only K/V cache; FlashDecoding split-KV partials
+ *                     merged by a log-sum-exp combine.
+ *   gqa_attn_prefill  a chunk of S_q query tokens, optionally causal with an
+ *                     offset (the chunk follows causal_offset cached tokens).
+ *
+ * Source of the operation: ADR-0060 "AHBM GQA Fused Attention Kernel
+ * (Llama3-70B)", kernbench2 revision 5a76ed4: "Algorithm lineage" (exact
+ * FlashAttention / FlashDecoding math), §0.5.3 INPUTS and §0.5.4 OUTPUTS (the
+ * kernel boundary), §3 "Per-tile op sequence", §4 "Reduction" (the merge),
+ * §5.2 (decode is unmasked) and §5.4 (causal tile classes).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers on the current HIP device and
+ *    must be 16-byte aligned.  Tensors are dense, row-major, head-major, with
+ *    the head dimension d innermost:
+ *        q (decode)   [B, H_q, d]          q (prefill)  [B, H_q, S_q, d]
+ *        k, v cache   [B, H_kv, kv_cap, d] (position j of a sequence = row j)
+ *        o            same shape as q, same dtype as q
+ *        lse          [B, H_q] (decode) / [B, H_q, S_q] (prefill), float32
+ *  - Query head h reads KV head h / (H_q / H_kv): the G = H_q / H_kv query
+ *    heads sharing a KV head are adjacent.
+ *  - Q and K are already RoPE-rotated, V is raw, and for decode the new
+ *    token's K/V row is already in the cache: the library only reads K/V
+ *    (preconditions P1-P4 of §0.5.1).
+ *  - scale multiplies q.k before the causal mask and the max (softmax_scale
+ *    of §0.5.3, normally 1/sqrt(d)).
+ *  - lse, when requested, is the natural-log log-sum-exp of the scaled,
+ *    visible scores of each query row.
+ *  - bf16 inputs are accumulated in float32; the output is rounded to the
+ *    input dtype with round-to-nearest-even.
+ *
+ * Ownership, threading, errors
+ * ----------------------------
+ *  - The caller owns every buffer (inputs, outputs, workspace).  The library
+ *    allocates, frees and synchronises nothing: it validates the arguments,
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream)
+ *    and returns.  Entry points are re-entrant; two calls that share a
+ *    workspace must not overlap in time.
+ *  - Every argument error is reported BEFORE anything is launched, and then
+ *    nothing has been written.  Launch failures return GQA_ERR_HIP.
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - Values stored in device memory (kv_lens) cannot be checked on the host:
+ *    they are a contract (see each entry point).
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_DTYPE_F32 = 0,   /* IEEE float32 */
+  GQA_DTYPE_BF16 = 1   /* bfloat16 (8-bit exponent, 7-bit mantissa) */
+} gqa_dtype_t;
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size or range  */
+  GQA_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+  GQA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required  */
+  GQA_ERR_HIP = 4           /* the HIP runtime rejected a launch           */
+} gqa_status_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* gqa_attn_status_string(int status);
+
+/* Version of this library as MAJOR*10000 + MINOR*100 + PATCH. */
+int gqa_attn_version(void);
+
+/*
+ * Number of keys each decode split (one workgroup's contiguous slice of one
+ * sequence) covers for these arguments: `chunk_tokens` itself when it is
+ * positive (it must then be a multiple of 128 for bf16, of 256 for f32), or
+ * the library's automatic choice when it is 0.  Splits are contiguous
+ * position blocks, the placement the pages require for prefill/decode
+ * sharing (§0 "CUBE Group", token-to-rank placement).  Returns a negative
+ * gqa_status_t on invalid arguments.
+ */
+int gqa_attn_decode_split_tokens(int B, int H_kv, int max_kv_len,
+                                 int chunk_tokens, int dtype);
+
+/*
+ * Device workspace (bytes) gqa_attn_decode needs: one unnormalised partial
+ * (m, l, O[d]) in float32 per (sequence, query head, split), the (m_i, l_i,
+ * O_i) of §4.  Returns 0 on invalid arguments.
+ */
+size_t gqa_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int d,
+                                       int max_kv_len, int chunk_tokens,
+                                       int dtype);
+
+/*
+ * Decode attention, T_q = 1 (§5.2 / §5.3, §4).
+ *
+ *   q        [B, H_q, d]             dtype
+ *   k_cache  [B, H_kv, kv_cap, d]    dtype, read-only
+ *   v_cache  [B, H_kv, kv_cap, d]    dtype, read-only
+ *   kv_lens  [B] int32, DEVICE memory: sequence b attends to its keys
+ *            0 .. kv_lens[b]-1.  Contract (not checked): 1 <= kv_lens[b] <=
+ *            max_kv_len.  Cache rows at or past kv_lens[b] are never read,
+ *            so they may hold anything (NaN included).
+ *   o        [B, H_q, d]             dtype, written
+ *   lse      [B, H_q] float32, written when non-NULL
+ *   max_kv_len   host-side upper bound of kv_lens, <= kv_cap; it sizes the
+ *                launch and the workspace.
+ *   chunk_tokens keys per split, 0 = automatic (see above).
+ *   workspace    device buffer of at least
+ *                gqa_attn_decode_workspace_bytes(...) bytes, 16-byte
+ *                aligned; its contents on entry do not matter.
+ *
+ * Each workgroup sweeps one split of one (sequence, KV head) with the G
+ * query heads folded into the matrix-core M dimension, writes the
+ * unnormalised partial, and a second kernel merges the partials and
+ * normalises once.  Requirements: d == 128 and G <= 16 (else
+ * GQA_ERR_UNSUPPORTED).
+ */
+int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* kv_lens, void* o, float* lse,
+                    int B, int H_q, int H_kv, int d, int kv_cap,
+                    int max_kv_len, float scale, int dtype, int chunk_tokens,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Prefill attention over a chunk of S_q queries (§5.4).
+ *
+ *   q     [B, H_q, S_q, d]       bf16
+ *   k, v  [B, H_kv, kv_cap, d]   bf16, read-only; rows 0 .. S_kv-1 are used
+ *   o     [B, H_q, S_q, d]       bf16, written
+ *   lse   [B, H_q, S_q] float32, written when non-NULL
+ *   causal = 1: query i sees keys j <= causal_offset + i (the chunk follows
+ *           causal_offset cached tokens); tiles wholly above the diagonal
+ *           are skipped, tiles wholly below are unmasked.  Requires
+ *           0 <= causal_offset and causal_offset + S_q <= S_kv.
+ *   causal = 0: every query sees all S_kv keys (causal_offset ignored).
+ *
+ * Requirements: dtype == GQA_DTYPE_BF16 and d == 128 (else
+ * GQA_ERR_UNSUPPORTED); S_kv <= kv_cap.
+ */
+int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o,
+                     float* lse, int B, int H_q, int H_kv, int d, int S_q,
+                     int S_kv, int kv_cap, int causal, int causal_offset,
+                     float scale, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -51,34 +51,35 @@ def kv_head_of(h: int, H_q: int, H_kv: int) -> int:
 def attend_rows(q_rows, k, v, scale: float, visible_len):
     """The definition: ``softmax(scale * q k^T over visible keys) v`` in fp64.
 
-    q_rows: ``[n, d]`` query rows of one query head.
-    k, v:   ``[L, d]`` keys and values of its KV head (row j = position j).
+    q_rows: ``[n, d]`` query rows of one query head (or of the G heads that
+    share one KV head).
+    k, v:   ``[L, d]`` keys and values of the KV head (row j = position j).
     visible_len: ``[n]`` ints; row i sees keys ``0 .. visible_len[i]-1``.
         Every entry must be >= 1 and <= L.
 
     Returns ``(o [n, d], lse [n])`` with ``lse = max_s + ln(sum exp(s - max_s))``
-    over the visible keys.  Keys beyond a row's visible length are never
-    read into the result, so NaN padding there cannot leak in.
+    over the visible keys.  Rows are independent; they are evaluated together
+    as matrix products.  Keys past the largest visible length are not read,
+    so NaN padding there cannot leak in.
     """
     q = np.asarray(q_rows, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
     vl = np.asarray(visible_len, dtype=np.int64).reshape(-1)
-    n, L = q.shape[0], k.shape[0]
+    n = q.shape[0]
     if vl.shape[0] != n:
         raise ValueError("visible_len must have one entry per query row")
-    if n and (vl.min() < 1 or vl.max() > L):
+    if n and (vl.min() < 1 or vl.max() > k.shape[0]):
         raise ValueError("visible lengths must lie in [1, L]")
-    o = np.empty((n, v.shape[1]), dtype=np.float64)
-    lse = np.empty(n, dtype=np.float64)
-    for i in range(n):
-        kv_i = k[: vl[i]]
-        s = float(scale) * (kv_i @ q[i])
-        mx = s.max()
-        w = np.exp(s - mx)
-        den = w.sum()
-        o[i] = (w @ v[: vl[i]]) / den
-        lse[i] = mx + np.log(den)
+    top = int(vl.max()) if n else 0
+    k = np.asarray(k[:top], dtype=np.float64)
+    v = np.asarray(v[:top], dtype=np.float64)
+    s = float(scale) * (q @ k.T)                       # [n, top]
+    visible = np.arange(top)[None, :] < vl[:, None]
+    s = np.where(visible, s, -np.inf)
+    mx = s.max(axis=1)
+    w = np.exp(s - mx[:, None])                        # hidden keys get 0
+    den = w.sum(axis=1)
+    o = (w @ v) / den[:, None]
+    lse = mx + np.log(den)
     return o, lse
 
 
@@ -88,7 +89,8 @@ def decode(q, k_cache, v_cache, kv_lens, scale: float):
     q: ``[B, H_q, d]``; k_cache, v_cache: ``[B, H_kv, kv_cap, d]``;
     kv_lens: ``[B]`` valid lengths (keys ``0 .. kv_lens[b]-1``).
     Decode is unmasked: the one new query attends to all past KV
-    (ADR-0060@5a76ed4 §5.2).  Returns ``(o [B, H_q, d], lse [B, H_q])``.
+    (ADR-0060@5a76ed4 §5.2).  The G query heads of a KV head are evaluated
+    together against it.  Returns ``(o [B, H_q, d], lse [B, H_q])``.
     """
     q = np.asarray(q)
     B, H_q, d = q.shape
@@ -98,12 +100,12 @@ def decode(q, k_cache, v_cache, kv_lens, scale: float):
     lse = np.empty((B, H_q), dtype=np.float64)
     for b in range(B):
         L = int(lens[b])
-        for h in range(H_q):
-            kv = kv_head_of(h, H_q, H_kv)
-            ob, lb = attend_rows(q[b, h][None, :], k_cache[b, kv, :L],
-                                 v_cache[b, kv, :L], scale, [L])
-            o[b, h] = ob[0]
-            lse[b, h] = lb[0]
+        for kv in range(H_kv):
+            heads = [h for h in range(H_q) if kv_head_of(h, H_q, H_kv) == kv]
+            ob, lb = attend_rows(q[b, heads], k_cache[b, kv, :L], v_cache[b, kv, :L],
+                                 scale, [L] * len(heads))
+            o[b, heads] = ob
+            lse[b, heads] = lb
     return o, lse
 
 
@@ -144,9 +146,11 @@ def prefill(q, k, v, S_kv: int, scale: float, causal: bool = True,
             kv = kv_head_of(int(h), H_q, H_kv)
             kk = np.asarray(k[b, kv, :top], dtype=np.float64)
             vv = np.asarray(v[b, kv, :top], dtype=np.float64)
-            ob, lb = attend_rows(q[b, h][rows], kk, vv, scale, vl)
-            o[b, hi] = ob
-            lse[b, hi] = lb
+            for r0 in range(0, len(rows), 256):       # bounded [rows, keys] block
+                r1 = min(r0 + 256, len(rows))
+                ob, lb = attend_rows(q[b, h][rows[r0:r1]], kk, vv, scale, vl[r0:r1])
+                o[b, hi, r0:r1] = ob
+                lse[b, hi, r0:r1] = lb
     return o, lse
 
 

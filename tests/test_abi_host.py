@@ -1,0 +1,130 @@
+"""C-ABI host checks that need no GPU: the library loads, exports every
+declared symbol, and rejects bad arguments before touching any pointer."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gqa_flashattention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="libgqa_attn.so not built")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+# Fake, 256-byte aligned device addresses: validation must reject the call
+# before any of them is dereferenced or handed to the runtime.
+P = ctypes.c_void_p(0x100000)
+P2 = ctypes.c_void_p(0x200000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(gqa_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_binding_agree():
+    decl = declared_functions()
+    assert decl, "no declarations parsed"
+    assert set(decl) == set(binding.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} not exported"
+
+
+def test_status_strings_and_version():
+    L = binding.lib()
+    for s in range(5):
+        assert L.gqa_attn_status_string(s)
+    assert L.gqa_attn_status_string(99) == b"unknown status"
+    assert L.gqa_attn_version() >= 100
+
+
+def test_split_tokens_rules():
+    L = binding.lib()
+    assert L.gqa_attn_decode_split_tokens(1, 1, 256, 0, F32) == 256
+    assert L.gqa_attn_decode_split_tokens(1, 1, 256, 128, F32) == -INVALID
+    assert L.gqa_attn_decode_split_tokens(1, 8, 32768, 384, BF16) == 384
+    assert L.gqa_attn_decode_split_tokens(1, 8, 32768, 100, BF16) == -INVALID
+    auto = L.gqa_attn_decode_split_tokens(1, 8, 32768, 0, BF16)
+    assert auto > 0 and auto % 128 == 0
+    assert L.gqa_attn_decode_split_tokens(1, 8, 100, 0, BF16) == 128   # tiny context
+    assert L.gqa_attn_decode_split_tokens(0, 8, 100, 0, BF16) == -INVALID
+    assert L.gqa_attn_decode_split_tokens(1, 8, 100, 0, 7) == -INVALID
+
+
+def test_workspace_bytes():
+    L = binding.lib()
+    n = L.gqa_attn_decode_workspace_bytes(1, 64, 8, 128, 32768, 256, BF16)
+    n_split = 32768 // 256
+    assert n >= 64 * n_split * (128 + 2) * 4
+    assert L.gqa_attn_decode_workspace_bytes(1, 64, 8, 64, 32768, 256, BF16) == 0
+    assert L.gqa_attn_decode_workspace_bytes(1, 63, 8, 128, 32768, 256, BF16) == 0
+
+
+def _decode(**kw):
+    a = dict(q=P, k=P, v=P, lens=P, o=P2, lse=None, B=1, H_q=8, H_kv=1, d=128, cap=256,
+             maxlen=256, scale=0.088, dtype=BF16, chunk=0, ws=P2, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return binding.lib().gqa_attn_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"],
+                                         a["B"], a["H_q"], a["H_kv"], a["d"], a["cap"],
+                                         a["maxlen"], a["scale"], a["dtype"], a["chunk"],
+                                         a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID),
+    (dict(k=None), INVALID),
+    (dict(lens=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(q=ctypes.c_void_p(0x100008)), INVALID),        # misaligned
+    (dict(lse=ctypes.c_void_p(0x100002)), INVALID),
+    (dict(B=0), INVALID),
+    (dict(H_kv=3), INVALID),                             # H_q % H_kv != 0
+    (dict(maxlen=257), INVALID),                         # > kv_cap
+    (dict(dtype=5), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(chunk=100), INVALID),
+    (dict(chunk=-128), INVALID),
+    (dict(d=64), UNSUPPORTED),
+    (dict(H_q=32, H_kv=1), UNSUPPORTED),                 # G > 16
+    (dict(ws=None), WORKSPACE),
+    (dict(wsb=16), WORKSPACE),
+])
+def test_decode_rejects_before_launch(kw, status):
+    assert _decode(**kw) == status
+
+
+def _prefill(**kw):
+    a = dict(q=P, k=P, v=P, o=P2, lse=None, B=1, H_q=8, H_kv=2, d=128, S_q=64, S_kv=128,
+             cap=128, causal=1, off=0, scale=0.088, dtype=BF16, stream=None)
+    a.update(kw)
+    return binding.lib().gqa_attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                          a["H_q"], a["H_kv"], a["d"], a["S_q"], a["S_kv"],
+                                          a["cap"], a["causal"], a["off"], a["scale"],
+                                          a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID),
+    (dict(v=ctypes.c_void_p(0x100004)), INVALID),
+    (dict(S_q=0), INVALID),
+    (dict(S_kv=129), INVALID),                           # > kv_cap
+    (dict(H_kv=3), INVALID),
+    (dict(causal=2), INVALID),
+    (dict(off=-1), INVALID),
+    (dict(off=65), INVALID),                             # offset + S_q > S_kv
+    (dict(scale=float("inf")), INVALID),
+    (dict(dtype=F32), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED),
+])
+def test_prefill_rejects_before_launch(kw, status):
+    assert _prefill(**kw) == status

@@ -17,16 +17,19 @@ SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__
 
 MUTANTS = {
     "head_map_modulo": ("return h // (H_q // H_kv)", "return h % H_kv"),
-    "dropped_scale": ("s = float(scale) * (kv_i @ q[i])", "s = (kv_i @ q[i])"),
+    "dropped_scale": ("s = float(scale) * (q @ k.T)                       # [n, top]",
+                      "s = (q @ k.T)"),
     "causal_off_by_one": ("return causal_offset + rows + 1", "return causal_offset + rows + 2"),
-    "max_sign": ("w = np.exp(s - mx)", "w = np.exp(s + mx)"),
-    "lse_dropped_max": ("lse[i] = mx + np.log(den)", "lse[i] = np.log(den)"),
-    "values_from_keys": ("o[i] = (w @ v[: vl[i]]) / den", "o[i] = (w @ k[: vl[i]]) / den"),
+    "max_sign": ("w = np.exp(s - mx[:, None])", "w = np.exp(s + mx[:, None])"),
+    "lse_dropped_max": ("lse = mx + np.log(den)\n    return o, lse", "lse = np.log(den)\n    return o, lse"),
+    "values_from_keys": ("o = (w @ v) / den[:, None]", "o = (w @ k) / den[:, None]"),
+    "mask_off_by_one": ("visible = np.arange(top)[None, :] < vl[:, None]",
+                        "visible = np.arange(top)[None, :] <= vl[:, None]"),
     "merge_weight_sign": ("sa = np.where(np.isneginf(m_a), 0.0, np.exp(m_a - m))",
                           "sa = np.where(np.isneginf(m_a), 0.0, np.exp(m - m_a))"),
     "sweep_no_rescale": ("o = o * corr[:, None] + p @ v[j0:j1]", "o = o + p @ v[j0:j1]"),
     "partial_unshifted": ("p = np.exp(s - m[:, None])", "p = np.exp(s)"),
-    "decode_drops_last_key": ("k_cache[b, kv, :L],\n", "k_cache[b, kv, :L - 1],\n"),
+    "decode_drops_last_key": ("v_cache[b, kv, :L],\n", "v_cache[b, kv, 1:L + 1],\n"),
     "keys_reversed": ("s = float(scale) * (q @ k.T)", "s = float(scale) * (q @ k[::-1].T)"),
     "visible_ignored": ("vis = np.arange(j0, j1)[None, :] < vl[:, None]",
                         "vis = np.arange(j0, j1)[None, :] < L + 0 * vl[:, None]"),
