@@ -1,0 +1,267 @@
+"""Benchmark of the GQA attention hot path on one MI355X.
+
+One step = one pass over both entry points on one batch of synthetic input:
+  * decode: Llama3-70B geometry (H_q=64, H_kv=8, d=128), batch 1, 32768 cached
+    keys, bf16 (the workload the headline metric is quoted on);
+  * prefill: causal, S_q = S_kv = 8192, same geometry, bf16.
+
+``value`` is decode KV throughput in GB/s: algorithmic bytes (K and V of the
+valid keys, plus Q and O) per decode call divided by the call's time, with
+inputs resident in HBM.  The decode K/V cache rotates over ``--kv-copies``
+distinct copies (default 4 x 128 MiB) so the 256 MB Infinity Cache cannot
+serve it from one call to the next.  The prefill figure (TFLOP/s over the
+exact causal visible-pair FLOPs) is reported in the ``prefill`` object.
+
+Timing uses HIP events on the stream the kernels run on, around every call
+of the timed region; warm-up calls are untimed.  ``cpu_baseline`` times the
+fp64 oracle on the host cores on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure (no sparsity)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--kv-copies", type=int, default=4)
+    ap.add_argument("--only", choices=["decode", "prefill", "both"], default="both",
+                    help="run one entry point only (for profiler runs)")
+    ap.add_argument("--chunk", type=int, default=0, help="decode keys per split (0 = auto)")
+    ap.add_argument("--decode-workload", default="decode_llama70b_32k",
+                    help="decode workload name (the headline is decode_llama70b_32k)")
+    ap.add_argument("--prefill-workload", default="prefill_causal_8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of each oracle sample")
+    return ap.parse_args()
+
+
+def traffic_from_profiles(kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    import hashlib
+    text = open(path).read()
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    table = json.loads(m.group(1))
+    ent = table.get(kernel)
+    if not ent:
+        return None
+    src = os.path.join(ROOT, "gqa_flashattention_amd", "csrc", ent["source"])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if sha != ent.get("source_sha256_16"):
+        return None
+    return ent["bytes_per_launch"]
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        return int(n)
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_decode(w, x_cpu, seconds):
+    """Oracle over whole decode calls of the workload, repeated to ~seconds."""
+    import numpy as np
+    import oracle
+    q, k, v = (x_cpu[n] for n in ("q", "k", "v"))
+    lens = np.array(w.lens)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(q, k, v, lens, w.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    gbs = w.decode_bytes() * reps / el / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{reps} full decode call(s) of {w.name} (B={w.B}, lens={list(w.lens)}, "
+                      f"all {w.H_q} heads) in {el:.1f} s, numpy fp64"}
+
+
+def cpu_baseline_prefill(w, x_cpu, seconds):
+    """Oracle on a seeded sample of query rows (all 64 heads), rows added in
+    blocks until ~seconds of CPU time; FLOPs counted exactly per row."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(7)
+    order = rng.permutation(w.S_q)
+    q, k, v = (x_cpu[n] for n in ("q", "k", "v"))
+    done, flops, t0 = 0, 0, time.perf_counter()
+    while done < w.S_q:
+        rows = np.sort(order[done:done + 64])
+        oracle.prefill(q, k, v, w.S_kv, w.scale, causal=w.causal, causal_offset=w.offset,
+                       rows=rows)
+        vis = oracle.prefill_visible_len(rows, w.S_kv, w.causal, w.offset)
+        flops += 4 * w.d * w.H_q * w.B * int(vis.sum())
+        done += len(rows)
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"{done} seeded query rows x {w.H_q} heads of {w.name} in {el:.1f} s, "
+                      f"numpy fp64"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gqa_flashattention_amd import binding as gq
+    from gqa_flashattention_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    wd = inputs.WORKLOADS[args.decode_workload]
+    wp = inputs.WORKLOADS[args.prefill_workload]
+    do_dec = args.only in ("decode", "both")
+    do_pre = args.only in ("prefill", "both")
+
+    # ---- inputs, resident in HBM before timing
+    if do_dec:
+        copies = [inputs.make_decode(wd, device=dev, seed=inputs.SEEDS[wd.name] + 100 * i)
+                  for i in range(max(1, args.kv_copies))]
+        need = gq.decode_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.max_kv_len, args.chunk,
+                                         gq.DTYPE_BF16)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        o_dec = torch.empty_like(copies[0]["q"])
+        chunk = gq.decode_split_tokens(wd.B, wd.H_kv, wd.max_kv_len, args.chunk, gq.DTYPE_BF16)
+    if do_pre:
+        xp = inputs.make_prefill(wp, device=dev)
+        o_pre = torch.empty_like(xp["q"])
+    torch.cuda.synchronize()
+
+    def decode_call(i):
+        x = copies[i % len(copies)]
+        gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=wd.max_kv_len,
+                  scale=wd.scale, chunk_tokens=args.chunk, out=o_dec, workspace=ws,
+                  stream=stream)
+
+    def prefill_call():
+        gq.prefill(xp["q"], xp["k"], xp["v"], S_kv=wp.S_kv, causal=wp.causal,
+                   causal_offset=wp.offset, scale=wp.scale, out=o_pre, stream=stream)
+
+    for i in range(args.warmup):
+        if do_dec:
+            decode_call(i)
+        if do_pre:
+            prefill_call()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        if do_dec:
+            decode_call(i)
+        ev[i][1].record(stream)
+        if do_pre:
+            prefill_call()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    pre_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
+    mean = lambda a: sum(a) / len(a)
+    median = lambda a: sorted(a)[len(a) // 2]
+
+    out = {
+        "metric": "decode KV GB/s (% HBM peak); causal prefill TFLOP/s (% bf16 MFMA peak)",
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean(step_ms), 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wd.name} + {wp.name}",
+                   "decode": {"B": wd.B, "H_q": wd.H_q, "H_kv": wd.H_kv, "d": wd.d,
+                              "kv_lens": list(wd.lens), "kv_copies": len(copies) if do_dec else 0,
+                              "keys_per_split": chunk if do_dec else None},
+                   "prefill": {"B": wp.B, "H_q": wp.H_q, "H_kv": wp.H_kv, "d": wp.d,
+                               "S_q": wp.S_q, "S_kv": wp.S_kv, "causal": wp.causal,
+                               "offset": wp.offset}},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if do_dec:
+        t_s = mean(dec_ms) / 1e3
+        gbs = wd.decode_bytes() / t_s / 1e9
+        out["value"] = round(gbs, 2)
+        out["decode"] = {"ms_mean": round(mean(dec_ms), 6), "ms_median": round(median(dec_ms), 6),
+                         "GB_s": round(gbs, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                         "bytes_per_call": wd.decode_bytes()}
+        tr = traffic_from_profiles("decode")
+        out["roofline"] = {"bound": "hbm", "kernel": "decode call: decode_partial_bf16_kernel + decode_combine_kernel",
+                           "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": tr}
+    else:
+        out["value"] = None
+    if do_pre:
+        t_s = mean(pre_ms) / 1e3
+        tf = wp.prefill_flops() / t_s / 1e12
+        out["prefill"] = {"value": round(tf, 2), "unit": "TFLOP/s",
+                          "ms_mean": round(mean(pre_ms), 6), "ms_median": round(median(pre_ms), 6),
+                          "flops_per_call": wp.prefill_flops(),
+                          "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel",
+                                       "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                       "traffic": traffic_from_profiles("prefill")}}
+        if not do_dec:
+            out["value"] = None
+
+    if not args.no_cpu_baseline:
+        import numpy as np  # noqa: F401
+        if do_dec:
+            xc = {n: copies[0][n].float().cpu().numpy() for n in ("q", "k", "v")}
+            out["cpu_baseline"] = cpu_baseline_decode(wd, xc, args.cpu_seconds)
+            del xc
+        if do_pre:
+            xc = {n: xp[n].float().cpu().numpy() for n in ("q", "k", "v")}
+            out["prefill"]["cpu_baseline"] = cpu_baseline_prefill(wp, xc, args.cpu_seconds)
+            del xc
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

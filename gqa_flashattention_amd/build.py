@@ -49,20 +49,20 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
     """Compile every HIP source and link ``libgqa_attn.so``; return its path."""
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -14,7 +14,6 @@ constexpr int kD = 128;
 constexpr int kMaxG = 16;          // query heads per KV head the decode MFMA tile holds
 constexpr int kF32Chunk = 256;     // keys per split of the fp32 decode path
 constexpr int kBf16ChunkQuantum = 128;  // 4 waves x 32-key blocks
-constexpr int kTargetSplits = 1024;     // ~4 workgroups per CU on 256 CUs
 constexpr size_t kWsAlign = 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -33,24 +32,27 @@ int split_tokens(int B, int H_kv, int max_kv_len, int chunk_tokens, int dtype) {
     if (chunk_tokens % kBf16ChunkQuantum != 0) return -GQA_ERR_INVALID_ARG;
     return chunk_tokens;
   }
-  const long long rows = (long long)B * H_kv * max_kv_len;
-  long long c = (rows + kTargetSplits - 1) / kTargetSplits;
+  // About 64 splits of the longest sequence, in multiples of 128 keys,
+  // between 256 and 1280 keys.  Measured on MI355X: 512 keys is best for one
+  // 32K-key sequence (partial traffic and the combine stay small), 1280 for
+  // a ragged batch up to 128K keys (more workgroups keep HBM busy).
+  long long c = ((long long)max_kv_len + 63) / 64;
   c = (c + kBf16ChunkQuantum - 1) / kBf16ChunkQuantum * kBf16ChunkQuantum;
+  if (c < 2 * kBf16ChunkQuantum) c = 2 * kBf16ChunkQuantum;
+  if (c > 10 * kBf16ChunkQuantum) c = 10 * kBf16ChunkQuantum;
   const long long cap = ((long long)max_kv_len + kBf16ChunkQuantum - 1) / kBf16ChunkQuantum * kBf16ChunkQuantum;
   if (c > cap) c = cap;
-  if (c > 16384) c = 16384;
-  if (c < kBf16ChunkQuantum) c = kBf16ChunkQuantum;
   return (int)c;
 }
 
+// Workspace: [partial O] [partial (m, l)], each region 256-byte aligned.
 struct WsLayout {
-  size_t o_bytes, ml_off, total;
+  size_t ml_off, total;
 };
 
 WsLayout ws_layout(int B, int H_q, int n_split) {
   WsLayout w;
-  w.o_bytes = (size_t)B * H_q * n_split * kD * sizeof(float);
-  w.ml_off = round_up(w.o_bytes, kWsAlign);
+  w.ml_off = round_up((size_t)B * H_q * n_split * kD * sizeof(float), kWsAlign);
   w.total = w.ml_off + round_up((size_t)B * H_q * n_split * 2 * sizeof(float), kWsAlign);
   return w;
 }

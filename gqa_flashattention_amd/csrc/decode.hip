@@ -18,6 +18,13 @@
 // permutes.  Scores live in the log2 domain (scale * log2(e) folded into one
 // multiply) so the exponentials are single v_exp_f32 instructions.  The 4
 // waves merge through LDS and the workgroup writes one partial.
+//
+// A second kernel merges the partials (one workgroup per sequence and query
+// head).  Merging inside the partial kernel -- the last workgroup to arrive
+// for a (sequence, KV head) merging the others' partials -- was measured
+// slower on MI355X: publishing partials across the 8 XCDs' separate L2s
+// costs either an L2 write-back per workgroup or agent-coherent accesses,
+// and the merge then runs serially on one CU at the end.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -31,9 +38,9 @@ constexpr int kWaves = 4;
 constexpr int kBlk = 32;  // keys per wave step
 
 // Loads of one 32-key block for one lane.
-//   kreg[sb][kb]: K row (key0 + 16*sb + l%16), d range 32*kb + 8*(l/16) .. +8
-//                 -> A operand of S^T tile sb, k-step kb.
-//   vreg[j]:      V row key(g, j), d range 8*(l%16) .. +8, where
+//   k[sb][kb]: K row (key0 + 16*sb + l%16), d range 32*kb + 8*(l/16) .. +8
+//              -> A operand of S^T tile sb, k-step kb.
+//   v[j]:      V row key(g, j), d range 8*(l%16) .. +8, where
 //                 key(g, j) = 4g + j (j < 4) or 16 + 4g + (j - 4) (j >= 4):
 //                 the keys this lane's P^T slots hold.
 struct Block {
@@ -322,42 +329,83 @@ __global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p)
   }
 }
 
-// Combine: one workgroup of 128 threads per (sequence, query head); thread
-// t owns output column d = t.  Merges the n_split(b) partials, normalises
-// once and rounds to the output dtype.
+// Online log-sum-exp merge of split partials, 16 at a time so that all of a
+// group's loads are in flight together.  (M, acc, lacc) is the running
+// state; a group is folded in with the merge rule of §4: rescale both sides
+// to the larger max and add.
+struct MergeAcc {
+  float M;
+  f32x4 acc;
+  float lacc;
+};
+
+__device__ __forceinline__ void merge_group(MergeAcc& st, const float* ml, const float* po,
+                                            int s0, int s1, int stride) {
+  constexpr int kGroup = 16;
+  float mv[kGroup], lv[kGroup];
+  f32x4 ov[kGroup];
+#pragma unroll
+  for (int u = 0; u < kGroup; ++u) {
+    const int s = s0 + u * stride;
+    const bool ok = s < s1;
+    const f32x2 m2 = ok ? *reinterpret_cast<const f32x2*>(ml + 2 * s) : f32x2{kNegInf, 0.f};
+    ov[u] = ok ? *reinterpret_cast<const f32x4*>(po + (size_t)s * kD) : f32x4{0.f, 0.f, 0.f, 0.f};
+    mv[u] = m2[0];
+    lv[u] = m2[1];
+  }
+  float gm = st.M;
+#pragma unroll
+  for (int u = 0; u < kGroup; ++u) gm = fmaxf(gm, mv[u]);
+  if (gm == kNegInf) return;
+  const float c = fast_exp2(st.M - gm);
+  st.acc *= c;
+  st.lacc *= c;
+#pragma unroll
+  for (int u = 0; u < kGroup; ++u) {
+    const float w = fast_exp2(mv[u] - gm);
+    st.acc += w * ov[u];
+    st.lacc += w * lv[u];
+  }
+  st.M = gm;
+}
+
+// Combine: one workgroup of 128 threads per (sequence, query head); 4 groups
+// of 32 threads take every 4th split, thread t covers output columns
+// 4*(t%32) .. +4, and the groups merge through LDS.  Normalises once and
+// rounds to the output dtype (the final O / l of §4).
 template <typename OutT>
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
   const int bh = blockIdx.x;
   const int b = bh / p.H_q;
   const int t = threadIdx.x;
+  const int grp = t >> 5;
+  const int d0 = (t & 31) * 4;
   const int L = p.kv_lens[b];
   const int ns = (L + p.chunk - 1) / p.chunk;
   const size_t part0 = (size_t)bh * p.n_split_max;
-  const float* ml = p.ws_ml + 2 * part0;
-  const float* po = p.ws_o + part0 * kD + t;
-  float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-  float acc = 0.f, lacc = 0.f;
-  int s = 0;
-  for (; s + 4 <= ns; s += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float w = fast_exp2(ml[2 * (s + u)] - M);
-      acc += w * po[(size_t)(s + u) * kD];
-      lacc += w * ml[2 * (s + u) + 1];
+  MergeAcc st{kNegInf, {0.f, 0.f, 0.f, 0.f}, 0.f};
+  for (int s0 = grp; s0 < ns; s0 += 64)
+    merge_group(st, p.ws_ml + 2 * part0, p.ws_o + part0 * kD + d0, s0, ns, 4);
+  __shared__ float sm[4], sl[4];
+  __shared__ f32x4 so[4][32];
+  if ((t & 31) == 0) { sm[grp] = st.M; sl[grp] = st.lacc; }
+  so[grp][t & 31] = st.acc;
+  __syncthreads();
+  if (grp == 0) {
+    float MM = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    for (int g = 0; g < 4; ++g) {
+      const float w = sm[g] == kNegInf ? 0.f : fast_exp2(sm[g] - MM);
+      a += w * so[g][t];
+      l += w * sl[g];
     }
+    const float inv = 1.f / l;
+    OutT* o = static_cast<OutT*>(p.o) + (size_t)bh * kD + d0;
+    for (int i = 0; i < 4; ++i) o[i] = (OutT)(a[i] * inv);
+    if (p.lse != nullptr && t == 0) p.lse[bh] = (MM + __log2f(l)) * kLn2;
   }
-  for (; s < ns; ++s) {
-    const float w = fast_exp2(ml[2 * s] - M);
-    acc += w * po[(size_t)s * kD];
-    lacc += w * ml[2 * s + 1];
-  }
-  const float val = acc / lacc;
-  OutT* o = static_cast<OutT*>(p.o) + (size_t)bh * kD;
-  o[t] = (OutT)val;
-  if (p.lse != nullptr && t == 0) p.lse[bh] = (M + __log2f(lacc)) * kLn2;
 }
-
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream) {
   dim3 grid(p.n_split_max, p.H_kv, p.B);
   if (bf16) {
@@ -367,11 +415,10 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 cgrid(p.B * p.H_q);
   if (bf16) {
-    hipLaunchKernelGGL(decode_combine_kernel<__bf16>, cgrid, dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<__bf16>, dim3(p.B * p.H_q), dim3(128), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(decode_combine_kernel<float>, cgrid, dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(p.B * p.H_q), dim3(128), 0, stream, p);
   }
   return hipGetLastError();
 }

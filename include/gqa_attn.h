@@ -94,8 +94,8 @@ int gqa_attn_decode_split_tokens(int B, int H_kv, int max_kv_len,
 
 /*
  * Device workspace (bytes) gqa_attn_decode needs: one unnormalised partial
- * (m, l, O[d]) in float32 per (sequence, query head, split), the (m_i, l_i,
- * O_i) of §4.  Returns 0 on invalid arguments.
+ * (m, l, O[d]) in float32 per (sequence, query head, split), the
+ * (m_i, l_i, O_i) of §4.  Returns 0 on invalid arguments.
  */
 size_t gqa_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int d,
                                        int max_kv_len, int chunk_tokens,
@@ -118,13 +118,14 @@ size_t gqa_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int d,
  *   chunk_tokens keys per split, 0 = automatic (see above).
  *   workspace    device buffer of at least
  *                gqa_attn_decode_workspace_bytes(...) bytes, 16-byte
- *                aligned; its contents on entry do not matter.
+ *                aligned; its contents on entry do not matter.  Calls
+ *                sharing a workspace must not overlap in time.
  *
- * Each workgroup sweeps one split of one (sequence, KV head) with the G
- * query heads folded into the matrix-core M dimension, writes the
- * unnormalised partial, and a second kernel merges the partials and
- * normalises once.  Requirements: d == 128 and G <= 16 (else
- * GQA_ERR_UNSUPPORTED).
+ * Two kernel launches on `stream`.  Each workgroup of the first sweeps one
+ * split of one (sequence, KV head) with the G query heads folded into the
+ * matrix-core tile and writes the unnormalised partial; the second merges
+ * the partials of each (sequence, query head) and normalises once.
+ * Requirements: d == 128 and G <= 16 (else GQA_ERR_UNSUPPORTED).
  */
 int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* kv_lens, void* o, float* lse,

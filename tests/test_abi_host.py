@@ -55,7 +55,8 @@ def test_split_tokens_rules():
     assert L.gqa_attn_decode_split_tokens(1, 8, 32768, 384, BF16) == 384
     assert L.gqa_attn_decode_split_tokens(1, 8, 32768, 100, BF16) == -INVALID
     auto = L.gqa_attn_decode_split_tokens(1, 8, 32768, 0, BF16)
-    assert auto > 0 and auto % 128 == 0
+    assert auto == 512
+    assert L.gqa_attn_decode_split_tokens(4, 8, 131072, 0, BF16) == 1280
     assert L.gqa_attn_decode_split_tokens(1, 8, 100, 0, BF16) == 128   # tiny context
     assert L.gqa_attn_decode_split_tokens(0, 8, 100, 0, BF16) == -INVALID
     assert L.gqa_attn_decode_split_tokens(1, 8, 100, 0, 7) == -INVALID

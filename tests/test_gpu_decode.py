@@ -132,18 +132,40 @@ def test_decode_zero_query_is_mean():
 
 
 def test_decode_workspace_reuse_and_stream():
-    """A caller-owned workspace reused across calls of different shapes."""
-    w = inputs.Workload("t", "decode", B=2, H_q=32, H_kv=4, d=128, dtype="bf16",
-                        lens=(3000, 1200), kv_cap=3000)
+    """One caller-owned workspace, filled with garbage first, reused across
+    calls of different shapes on a side stream."""
     banner("decode_workspace_reuse")
-    x = inputs.make_decode(w, device=DEV, seed=14)
     need = gq.decode_workspace_bytes(2, 32, 4, 128, 3000, 0, gq.DTYPE_BF16)
-    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)   # garbage content
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
     s = torch.cuda.Stream()
-    with torch.cuda.stream(s):
-        o = gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], scale=w.scale, workspace=ws,
-                      stream=s)
-    s.synchronize()
-    ref_o, _ = _oracle(x, w)
-    for b in range(2):
-        check_bf16(np32(o[b]), ref_o[b], f"ws reuse seq {b}")
+    for lens, H_q, H_kv in (((3000, 1200), 32, 4), ((700, 2999), 16, 2), ((3000, 1), 32, 4)):
+        w = inputs.Workload("t", "decode", B=2, H_q=H_q, H_kv=H_kv, d=128, dtype="bf16",
+                            lens=lens, kv_cap=3000)
+        x = inputs.make_decode(w, device=DEV, seed=14 + H_q)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            o = gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], scale=w.scale, workspace=ws,
+                          stream=s)
+        s.synchronize()
+        ref_o, _ = _oracle(x, w)
+        for b in range(2):
+            check_bf16(np32(o[b]), ref_o[b], f"ws reuse {lens} seq {b}")
+
+
+def test_decode_alternating_inputs_bitwise():
+    """Back-to-back calls alternating between four inputs on one workspace:
+    every output equals its own first result bitwise (no stale partials)."""
+    w = inputs.WORKLOADS["decode_llama70b_32k"]
+    banner("decode_alternating", w.name)
+    xs = [inputs.make_decode(w, device=DEV, seed=40 + i) for i in range(4)]
+    need = gq.decode_workspace_bytes(1, 64, 8, 128, 32768, 0, gq.DTYPE_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    refs = [gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], scale=w.scale, workspace=ws).clone()
+            for x in xs]
+    outs = [torch.empty_like(refs[0]) for _ in range(64)]
+    for i in range(64):
+        x = xs[i % 4]
+        gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], scale=w.scale, out=outs[i], workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(64):
+        assert torch.equal(outs[i], refs[i % 4]), f"call {i} differs"
