@@ -147,8 +147,10 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float
   if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16) return GQA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
   if (d != kD || dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
-  const long long n_qblk = ((long long)S_q + gqa::kPrefillBlockM - 1) / gqa::kPrefillBlockM;
-  if (n_qblk * B * H_q > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
+  const int hpw = gqa::prefill_heads_per_wg(H_q / H_kv);
+  const long long rows_per_wg = gqa::prefill_rows_per_wg() / hpw;
+  const long long n_qblk = ((long long)S_q + rows_per_wg - 1) / rows_per_wg;
+  if (n_qblk * B * H_kv * ((H_q / H_kv) / hpw) > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
 
   gqa::PrefillParams p;
   p.q = q;
@@ -165,8 +167,10 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float
   p.kv_cap = kv_cap;
   p.causal = causal;
   p.offset = causal ? causal_offset : 0;
+  p.heads_per_wg = hpw;
   p.n_qblk = (int)n_qblk;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  p.q_negate = scale < 0.f;
+  p.scale_log2 = fabsf(scale) * 1.4426950408889634f;
   hipError_t e = gqa::launch_prefill(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }

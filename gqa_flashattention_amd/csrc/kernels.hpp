@@ -30,14 +30,18 @@ struct PrefillParams {
   float* lse;           // [B, H_q, S_q] or null
   int B, H_q, H_kv, G, S_q, S_kv, kv_cap;
   int causal, offset;
-  int n_qblk;           // ceil(S_q / block rows)
-  float scale_log2;
+  int heads_per_wg;     // query heads of one KV group per workgroup: gcd(G, waves)
+  int n_qblk;           // position blocks: ceil(S_q / (32 * waves / heads_per_wg))
+  int q_negate;         // 1 when the softmax scale is negative (Q's sign is flipped)
+  float scale_log2;     // |scale| * log2(e)
 };
 
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
-// Rows of queries one prefill workgroup covers.
-constexpr int kPrefillBlockM = 128;
+// Query heads of one KV group a prefill workgroup covers, and the query rows
+// (heads x positions) of one workgroup.
+int prefill_heads_per_wg(int G);
+int prefill_rows_per_wg();
 
 }  // namespace gqa

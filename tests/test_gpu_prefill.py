@@ -78,6 +78,10 @@ SMALL = [
     (2, 8, 1, 200, 333, 333, False, 0),
     (1, 64, 8, 384, 384, 384, True, 0),
     (1, 8, 8, 1, 5000, 5000, True, 4999),
+    (1, 16, 8, 150, 150, 150, True, 0),          # G = 2
+    (1, 12, 2, 100, 400, 400, True, 300),        # G = 6: 2 heads x 4 position blocks
+    (1, 32, 2, 70, 70, 70, True, 0),             # G = 16: two head groups
+    (1, 8, 1, 96, 2000, 2048, False, 0),         # non-causal, long keys, ragged tail
 ]
 
 
@@ -128,3 +132,20 @@ def test_prefill_row_matches_decode():
         ro, _ = oracle.decode(np32(qd), np32(x["k"]), np32(x["v"]), np.array([L]), w.scale)
         check_bf16(np32(o[:, :, i]), ro, f"prefill row {i}")
         check_bf16(np32(od), ro, f"decode len {L}")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.3])
+def test_prefill_scale_sign_and_zero(scale):
+    """Negative scale (applied by flipping Q's sign), zero scale (uniform
+    weights over the visible keys) and a large scale, causal with an offset."""
+    w = inputs.Workload("t", "prefill", B=1, H_q=16, H_kv=2, d=128, dtype="bf16", S_q=90,
+                        S_kv=200, causal=True, offset=110)
+    banner("prefill_scale", scale)
+    x = inputs.make_prefill(w, device=DEV, seed=23)
+    o, lse = gq.prefill(x["q"], x["k"], x["v"], S_kv=200, causal=True, causal_offset=110,
+                        scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill(np32(x["q"]), np32(x["k"]), np32(x["v"]), 200, scale, causal=True,
+                            causal_offset=110)
+    check_bf16(np32(o[0]), ro[0], f"scale {scale}")
+    check_lse(np32(lse), rl, f"scale {scale}", LSE_ATOL_BF16)
