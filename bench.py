@@ -50,13 +50,30 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of each oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device copy 5 times (calibrates the HBM "
+                         "byte counters under rocprofv3 --pmc)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """Plain device-to-device copy of a known size, for counter calibration."""
+    import torch
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n, "bytes_written": n, "copies": 5}),
+          flush=True)
 
 
 def traffic_from_profiles(kernel: str):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_decode_llama70b_32k_prefill_causal_8k.md")
     if not os.path.exists(path):
         return None
     import hashlib
@@ -95,7 +112,7 @@ def cpu_baseline_decode(w, x_cpu, seconds):
         oracle.decode(q, k, v, lens, w.scale)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 50:
+        if el >= seconds or reps >= 1000:
             break
     gbs = w.decode_bytes() * reps / el / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle",
@@ -130,8 +147,11 @@ def cpu_baseline_prefill(w, x_cpu, seconds):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not "
               "supported (the multi-GPU sharding is described, not built)", file=sys.stderr)
         sys.exit(2)
 
@@ -165,15 +185,15 @@ def main():
         o_pre = torch.empty_like(xp["q"])
     torch.cuda.synchronize()
 
-    def decode_call(i):
-        x = copies[i % len(copies)]
-        gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=wd.max_kv_len,
-                  scale=wd.scale, chunk_tokens=args.chunk, out=o_dec, workspace=ws,
-                  stream=stream)
-
     def prefill_call():
         gq.prefill(xp["q"], xp["k"], xp["v"], S_kv=wp.S_kv, causal=wp.causal,
                    causal_offset=wp.offset, scale=wp.scale, out=o_pre, stream=stream)
+
+    def decode_call(i, phase="both"):
+        x = copies[i % len(copies)]
+        gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=wd.max_kv_len,
+                  scale=wd.scale, chunk_tokens=args.chunk, out=o_dec, workspace=ws,
+                  stream=stream, phase=phase)
 
     for i in range(args.warmup):
         if do_dec:
@@ -182,8 +202,13 @@ def main():
             prefill_call()
     torch.cuda.synchronize()
 
+    # Timed region.  (1) K steps: one gqa_attn_decode call and one prefill
+    # call each, HIP events around every call.  (2) The decode split kernel
+    # alone (gqa_attn_decode_partial), K back-to-back launches between two
+    # events, for its per-launch duration (the roofline kernel).
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    kp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(K):
@@ -194,16 +219,23 @@ def main():
         if do_pre:
             prefill_call()
         ev[i][2].record(stream)
+    if do_dec:
+        kp[0].record(stream)
+        for i in range(K):
+            decode_call(i, "partial")
+        kp[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
     pre_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
     step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
+    part_us = kp[0].elapsed_time(kp[1]) * 1e3 / K if do_dec else None
     mean = lambda a: sum(a) / len(a)
     median = lambda a: sorted(a)[len(a) // 2]
 
     out = {
         "metric": "decode KV GB/s (% HBM peak); causal prefill TFLOP/s (% bf16 MFMA peak)",
+        "value": None,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
@@ -226,16 +258,20 @@ def main():
     if do_dec:
         t_s = mean(dec_ms) / 1e3
         gbs = wd.decode_bytes() / t_s / 1e9
+        # Split kernel's algorithmic bytes: K and V of the valid keys plus Q.
+        part_bytes = wd.kv_bytes() + wd.B * wd.H_q * wd.d * wd.elem_bytes
+        part_gbs = part_bytes / (part_us / 1e6) / 1e9
         out["value"] = round(gbs, 2)
         out["decode"] = {"ms_mean": round(mean(dec_ms), 6), "ms_median": round(median(dec_ms), 6),
                          "GB_s": round(gbs, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                         "bytes_per_call": wd.decode_bytes()}
-        tr = traffic_from_profiles("decode")
-        out["roofline"] = {"bound": "hbm", "kernel": "decode call: decode_partial_bf16_kernel + decode_combine_kernel",
-                           "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": tr}
-    else:
-        out["value"] = None
+                         "bytes_per_call": wd.decode_bytes(),
+                         "partial_kernel_us_mean": round(part_us, 3)}
+        out["roofline"] = {"bound": "hbm", "kernel": "decode_partial_bf16_kernel",
+                           "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(part_gbs / HBM_PEAK_GBS, 4),
+                           "traffic": traffic_from_profiles("decode_partial"),
+                           "algorithmic_bytes_per_launch": part_bytes,
+                           "launch_us_mean": round(part_us, 3)}
     if do_pre:
         t_s = mean(pre_ms) / 1e3
         tf = wp.prefill_flops() / t_s / 1e12
@@ -245,9 +281,8 @@ def main():
                           "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel",
                                        "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                                       "traffic": traffic_from_profiles("prefill")}}
-        if not do_dec:
-            out["value"] = None
+                                       "traffic": traffic_from_profiles("prefill"),
+                                       "launch_us_mean": round(mean(pre_ms) * 1e3, 3)}}
 
     if not args.no_cpu_baseline:
         import numpy as np  # noqa: F401

@@ -32,6 +32,10 @@ SIGNATURES = {
     "gqa_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "gqa_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                              _i, _vp, _sz, _vp]),
+    "gqa_attn_decode_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                                     _i, _i, _vp, _sz, _vp]),
+    "gqa_attn_decode_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                                     _i, _i, _vp, _sz, _vp]),
     "gqa_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                               _f, _i, _vp]),
 }
@@ -109,12 +113,14 @@ def decode_workspace_bytes(B, H_q, H_kv, d, max_kv_len, chunk_tokens=0, dtype=DT
 
 
 def decode(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chunk_tokens=0,
-           return_lse=False, out=None, lse=None, workspace=None, stream=None):
+           return_lse=False, out=None, lse=None, workspace=None, stream=None, phase="both"):
     """``gqa_attn_decode`` on torch tensors.
 
     q ``[B,H_q,d]``, k_cache/v_cache ``[B,H_kv,kv_cap,d]`` (same dtype, bf16 or
     fp32), kv_lens ``[B]`` int32 on the device.  ``max_kv_len`` defaults to
-    ``kv_cap``.  Returns ``o`` (and ``lse`` when ``return_lse``).
+    ``kv_cap``.  ``phase`` = "partial" or "combine" issues only that launch
+    (``gqa_attn_decode_partial`` / ``_combine``; pass the same ``workspace``
+    to both).  Returns ``o`` (and ``lse`` when ``return_lse``).
     """
     _require_gpu(q, k_cache, v_cache, kv_lens)
     B, H_q, d = q.shape
@@ -131,11 +137,13 @@ def decode(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chunk_toke
     need = decode_workspace_bytes(B, H_q, H_kv, d, max_kv_len, chunk_tokens, dt)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    st = lib().gqa_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens), _ptr(out),
-                               _ptr(lse) if return_lse else None, B, H_q, H_kv, d, kv_cap,
-                               max_kv_len, scale, dt, chunk_tokens, _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream))
-    _check(st, "gqa_attn_decode")
+    fn = {"both": "gqa_attn_decode", "partial": "gqa_attn_decode_partial",
+          "combine": "gqa_attn_decode_combine"}[phase]
+    st = getattr(lib(), fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens), _ptr(out),
+                            _ptr(lse) if return_lse else None, B, H_q, H_kv, d, kv_cap,
+                            max_kv_len, scale, dt, chunk_tokens, _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, fn)
     return (out, lse) if return_lse else out
 
 

@@ -87,10 +87,11 @@ size_t gqa_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int d, int max_
   return ws_layout(B, H_q, n_split).total;
 }
 
-int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
-                    int d, int kv_cap, int max_kv_len, float scale, int dtype, int chunk_tokens,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+static int decode_phases(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
+                         int d, int kv_cap, int max_kv_len, float scale, int dtype,
+                         int chunk_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                         int phases) {
   if (!q || !k_cache || !v_cache || !kv_lens || !o) return GQA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return GQA_ERR_INVALID_ARG;
@@ -128,8 +129,38 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
   p.chunk = chunk;
   p.n_split_max = n_split;
   p.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = gqa::launch_decode(p, dtype == GQA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  hipError_t e = gqa::launch_decode(p, dtype == GQA_DTYPE_BF16, static_cast<hipStream_t>(stream),
+                                    phases);
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
+                    int d, int kv_cap, int max_kv_len, float scale, int dtype, int chunk_tokens,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_phases(q, k_cache, v_cache, kv_lens, o, lse, B, H_q, H_kv, d, kv_cap, max_kv_len,
+                       scale, dtype, chunk_tokens, workspace, workspace_bytes, stream,
+                       gqa::kDecodePartial | gqa::kDecodeCombine);
+}
+
+int gqa_attn_decode_partial(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* kv_lens, void* o, float* lse, int B, int H_q,
+                            int H_kv, int d, int kv_cap, int max_kv_len, float scale, int dtype,
+                            int chunk_tokens, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return decode_phases(q, k_cache, v_cache, kv_lens, o, lse, B, H_q, H_kv, d, kv_cap, max_kv_len,
+                       scale, dtype, chunk_tokens, workspace, workspace_bytes, stream,
+                       gqa::kDecodePartial);
+}
+
+int gqa_attn_decode_combine(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* kv_lens, void* o, float* lse, int B, int H_q,
+                            int H_kv, int d, int kv_cap, int max_kv_len, float scale, int dtype,
+                            int chunk_tokens, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return decode_phases(q, k_cache, v_cache, kv_lens, o, lse, B, H_q, H_kv, d, kv_cap, max_kv_len,
+                       scale, dtype, chunk_tokens, workspace, workspace_bytes, stream,
+                       gqa::kDecodeCombine);
 }
 
 int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,

@@ -406,19 +406,23 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
     if (p.lse != nullptr && t == 0) p.lse[bh] = (MM + __log2f(l)) * kLn2;
   }
 }
-hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream) {
-  dim3 grid(p.n_split_max, p.H_kv, p.B);
-  if (bf16) {
-    hipLaunchKernelGGL(decode_partial_bf16_kernel, grid, dim3(256), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(decode_partial_f32_kernel, grid, dim3(256), 0, stream, p);
+hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, int phases) {
+  if (phases & kDecodePartial) {
+    dim3 grid(p.n_split_max, p.H_kv, p.B);
+    if (bf16) {
+      hipLaunchKernelGGL(decode_partial_bf16_kernel, grid, dim3(256), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL(decode_partial_f32_kernel, grid, dim3(256), 0, stream, p);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (bf16) {
-    hipLaunchKernelGGL(decode_combine_kernel<__bf16>, dim3(p.B * p.H_q), dim3(128), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(p.B * p.H_q), dim3(128), 0, stream, p);
+  if (phases & kDecodeCombine) {
+    if (bf16) {
+      hipLaunchKernelGGL(decode_combine_kernel<__bf16>, dim3(p.B * p.H_q), dim3(128), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(p.B * p.H_q), dim3(128), 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

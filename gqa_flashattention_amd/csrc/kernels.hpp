@@ -36,7 +36,10 @@ struct PrefillParams {
   float scale_log2;     // |scale| * log2(e)
 };
 
-hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream);
+// Decode launches: the split partial kernel, the combine kernel, or both.
+constexpr int kDecodePartial = 1;
+constexpr int kDecodeCombine = 2;
+hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, int phases);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
 // Query heads of one KV group a prefill workgroup covers, and the query rows

@@ -69,7 +69,7 @@ typedef enum {
 typedef enum {
   GQA_OK = 0,
   GQA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size or range  */
-  GQA_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+  GQA_ERR_UNSUPPORTED = 2,  /* valid request the library does not implement */
   GQA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required  */
   GQA_ERR_HIP = 4           /* the HIP runtime rejected a launch           */
 } gqa_status_t;
@@ -132,6 +132,28 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                     int B, int H_q, int H_kv, int d, int kv_cap,
                     int max_kv_len, float scale, int dtype, int chunk_tokens,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two launches of gqa_attn_decode, separately: _partial runs the split
+ * sweeps and writes the partials into `workspace`; _combine merges them
+ * into `o` (and `lse`).  Both take exactly the arguments of
+ * gqa_attn_decode and validate them the same way; issuing _partial then
+ * _combine on one stream with the same arguments is gqa_attn_decode.  For
+ * callers that time or schedule the two kernels apart.  _partial does not
+ * touch `o`/`lse`; _combine reads only `kv_lens` and the workspace.
+ */
+int gqa_attn_decode_partial(const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* kv_lens,
+                            void* o, float* lse, int B, int H_q, int H_kv,
+                            int d, int kv_cap, int max_kv_len, float scale,
+                            int dtype, int chunk_tokens, void* workspace,
+                            size_t workspace_bytes, void* stream);
+int gqa_attn_decode_combine(const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* kv_lens,
+                            void* o, float* lse, int B, int H_q, int H_kv,
+                            int d, int kv_cap, int max_kv_len, float scale,
+                            int dtype, int chunk_tokens, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * Prefill attention over a chunk of S_q queries (§5.4).

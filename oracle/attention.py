@@ -17,7 +17,7 @@ normalisation and the per-tile streaming update -- so that tests can check,
 in fp64, that composing them gives the definition for any partition and any
 tile size.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   * query head ``h`` reads KV head ``h // G`` (the G query rows of one KV head
     are stacked contiguously, ADR-0060@5a76ed4 §0 "CUBE Group" and §0.5.3
     INPUTS, where Q is ``[G, T_q, d]`` per KV head);

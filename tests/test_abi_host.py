@@ -71,11 +71,11 @@ def test_workspace_bytes():
     assert L.gqa_attn_decode_workspace_bytes(1, 63, 8, 128, 32768, 256, BF16) == 0
 
 
-def _decode(**kw):
+def _decode(fn="gqa_attn_decode", **kw):
     a = dict(q=P, k=P, v=P, lens=P, o=P2, lse=None, B=1, H_q=8, H_kv=1, d=128, cap=256,
              maxlen=256, scale=0.088, dtype=BF16, chunk=0, ws=P2, wsb=1 << 30, stream=None)
     a.update(kw)
-    return binding.lib().gqa_attn_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"],
+    return getattr(binding.lib(), fn)(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"],
                                          a["B"], a["H_q"], a["H_kv"], a["d"], a["cap"],
                                          a["maxlen"], a["scale"], a["dtype"], a["chunk"],
                                          a["ws"], a["wsb"], a["stream"])
@@ -100,8 +100,10 @@ def _decode(**kw):
     (dict(ws=None), WORKSPACE),
     (dict(wsb=16), WORKSPACE),
 ])
-def test_decode_rejects_before_launch(kw, status):
-    assert _decode(**kw) == status
+@pytest.mark.parametrize("fn", ["gqa_attn_decode", "gqa_attn_decode_partial",
+                                "gqa_attn_decode_combine"])
+def test_decode_rejects_before_launch(kw, status, fn):
+    assert _decode(fn, **kw) == status
 
 
 def _prefill(**kw):

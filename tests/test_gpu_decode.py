@@ -169,3 +169,23 @@ def test_decode_alternating_inputs_bitwise():
     torch.cuda.synchronize()
     for i in range(64):
         assert torch.equal(outs[i], refs[i % 4]), f"call {i} differs"
+
+
+def test_decode_phases_equal_one_call():
+    """gqa_attn_decode_partial then _combine on one stream is gqa_attn_decode."""
+    w = inputs.Workload("t", "decode", B=3, H_q=64, H_kv=8, d=128, dtype="bf16",
+                        lens=(4000, 70, 2500), kv_cap=4096)
+    banner("decode_phases")
+    x = inputs.make_decode(w, device=DEV, seed=31)
+    ws = torch.empty(gq.decode_workspace_bytes(3, 64, 8, 128, 4000, 0, gq.DTYPE_BF16),
+                     dtype=torch.uint8, device=DEV)
+    one, l1 = gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=4000, scale=w.scale,
+                        return_lse=True, workspace=ws)
+    two = torch.empty_like(one)
+    l2 = torch.empty_like(l1)
+    gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=4000, scale=w.scale,
+              return_lse=True, out=two, lse=l2, workspace=ws, phase="partial")
+    gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=4000, scale=w.scale,
+              return_lse=True, out=two, lse=l2, workspace=ws, phase="combine")
+    torch.cuda.synchronize()
+    assert torch.equal(one, two) and torch.equal(l1, l2)
