@@ -44,6 +44,8 @@
 // stay in one XCD's L2; query blocks go heaviest (longest causal prefix)
 // first.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -56,15 +58,27 @@ constexpr int kBN = 64;              // keys per tile
 constexpr int kWaves = 8;            // waves per workgroup: two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileElems = kBN * kD; // 16 KiB of bf16 per tile, unpadded
-constexpr int kBufs = 3;
+constexpr int kBufs = 4;              // K and V tile rings (tile t in buffer t % 4)
+
 constexpr float kResetGap = 64.f;    // log2 units
 constexpr float kRefBelow = 32.f;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+constexpr int kTileBytes = kTileElems * 2;
+
+// 32-bit LDS address of a shared-memory object, and back.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(3))) T* lds_ptr(unsigned a) {
+  return (const __attribute__((address_space(3))) T*)(uintptr_t)a;
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr16(unsigned a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a);
 }
 
 // Physical 16-byte piece of logical piece `pc` (0..15) in tile row `row`.
@@ -78,6 +92,9 @@ struct Tile16 {
 struct PTile {
   bf16x8 p[4];   // P of 16-key step st: keys 16*st + {0..3, 8..11} + 4*h2, query c
 };
+
+template <int N>
+using Int = std::integral_constant<int, N>;
 
 }  // namespace
 
@@ -143,39 +160,79 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     }
   }
 
+  // Per-lane LDS byte addresses of the MFMA operands in buffer 0; other
+  // buffers and sub-blocks are immediate offsets (all below 64 KiB).
+  //  K (A of S^T), k-step ks, sub-tile mt: row 32*mt + c, logical piece
+  //    2*ks + h2; row + 32 has the same swizzle, so mt adds 8 KiB.
+  //  V (A of O^T, transposed read), key step st, d-tile dt: rows
+  //    r0 = 16*st + 4*h2 + t16/4 and r0 + 8, element e = 32*dt +
+  //    16*(gamma&1) + 4*(t16&3); r0 & 3 does not depend on st, so st adds
+  //    4 KiB and the second row 2 KiB.
+  // The addresses are hidden from the compiler so that it cannot fold the
+  // arrays' base into the 16-bit offsets (which would overflow them).
+  unsigned kaddr[8], vaddr[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    kaddr[ks] = lds_addr(&sK[0][0]) + c * 256 + 16 * k_swz(c, 2 * ks + h2);
+    asm volatile("" : "+v"(kaddr[ks]));
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int r0 = 4 * h2 + (t16 >> 2);
+    const int e = 32 * dt + 16 * (gamma & 1) + 4 * (t16 & 3);
+    vaddr[dt] = lds_addr(&sV[0][0]) + r0 * 256 + 16 * v_swz(r0, e >> 3) + 2 * (e & 7);
+    asm volatile("" : "+v"(vaddr[dt]));
+  }
+  auto k_opnd = [&](int buf, int mt, int ks) -> bf16x8 {
+    return *lds_ptr<bf16x8>(kaddr[ks] + kTileBytes * buf + 8192 * mt);
+  };
+  auto v_opnd = [&](int buf, int st, int dt) -> bf16x8 {
+    const unsigned a = vaddr[dt] + kTileBytes * buf + 4096 * st;
+    const u32x2 w0 = __builtin_bit_cast(u32x2, lds_read_tr16(a));
+    const u32x2 w1 = __builtin_bit_cast(u32x2, lds_read_tr16(a + 2048));
+    const u32x4 av = {w0[0], w0[1], w1[0], w1[1]};
+    return as_bf16x8(av);
+  };
+
   // Direct global -> LDS tile load: the waves split the 16 row groups of 4
   // rows; one 1 KiB instruction fills a group, lane l landing at physical
   // piece l%16 of row 4*group + l/16 and fetching the logical piece that
-  // belongs there.  Rows
-  // past S_kv re-read the last valid row (finite data; those keys are
-  // masked and their V rows get weight 0).
-  auto tile_load = [&](__bf16* buf, const __bf16* g, int tile, bool is_v) {
-    constexpr int kInsts = kBN / 4 / kWaves;   // 1 KiB (4-row) loads per wave
+  // belongs there.  Per lane, the byte offset inside a tile is fixed; rows
+  // past S_kv (last tile only) re-read the last valid row (finite data;
+  // those keys are masked and their V rows get weight 0).
+  constexpr int kInsts = kBN / 4 / kWaves;   // 1 KiB (4-row) loads per wave
+  int ld_off[2][kInsts];                     // [K, V][instruction]
+#pragma unroll
+  for (int i = 0; i < kInsts; ++i) {
+    const int row = 4 * (kInsts * wave + i) + (lane >> 4);
+    ld_off[0][i] = row * (kD * 2) + 16 * k_swz(row, lane & 15);   // XOR is an involution
+    ld_off[1][i] = row * (kD * 2) + 16 * v_swz(row, lane & 15);
+  }
+  auto tile_load = [&](__bf16* buf, const __bf16* g, int tile, int kv) {
+    const char* base = reinterpret_cast<const char*>(g) + (size_t)tile * (kBN * kD * 2);
+    const bool tail = tile * kBN + kBN > p.S_kv;
 #pragma unroll
     for (int i = 0; i < kInsts; ++i) {
       const int row0 = 4 * (kInsts * wave + i);
-      const int row = row0 + (lane >> 4);
-      const int phys = lane & 15;
-      const int logical = is_v ? v_swz(row, phys) : k_swz(row, phys);   // XOR is an involution
-      const int key = min(tile * kBN + row, p.S_kv - 1);
-      const __bf16* src = g + (size_t)key * kD + logical * 8;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + row0 * kD), 16, 0, 0);
+      int off = ld_off[kv][i];
+      if (tail) {
+        const int key = min(tile * kBN + row0 + (lane >> 4), p.S_kv - 1);
+        off = (key - tile * kBN) * (kD * 2) + (off & (kD * 2 - 1));
+      }
+      __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(buf + row0 * kD), 16, 0, 0);
     }
   };
 
   // S^T of one tile from K buffer `kb`.
-  auto compute_s = [&](Tile16& T, const __bf16* kb) {
+  auto compute_s = [&](Tile16& T, int kb) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int row = 32 * mt + c;
-      const __bf16* kr = kb + row * kD;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 8 * k_swz(row, 2 * ks + h2));
         const f32x16 zero = {};
-        T.s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], ks ? T.s[mt] : zero, 0, 0, 0);
+        T.s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_opnd(kb, mt, ks), qb[ks],
+                                                          ks ? T.s[mt] : zero, 0, 0, 0);
       }
-    }
   };
 
   f32x16 o[4];
@@ -187,59 +244,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // O^T += V^T . P^T for one tile from V buffer `vb`.  Lane (gamma, t16)
   // supplies the address of row r0 + t16/4, d = 32*dt + 16*(gamma&1) +
   // 4*(t16&3) .. +4, and receives V^T column d = 32*dt + 16*(gamma&1) + t16.
-  auto pv = [&](const PTile& P, const __bf16* vb) {
+  auto pv = [&](const PTile& P, int vb) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int r0 = 16 * st + 4 * h2 + (t16 >> 2);
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int e = 32 * dt + 16 * (gamma & 1) + 4 * (t16 & 3);   // element within the row
-        const int pc = e >> 3;
-        const int off = e & 7;
-        const s16x4 x0 = lds_read_tr16(vb + r0 * kD + 8 * v_swz(r0, pc) + off);
-        const s16x4 x1 = lds_read_tr16(vb + (r0 + 8) * kD + 8 * v_swz(r0 + 8, pc) + off);
-        u32x4 av;
-        av[0] = __builtin_bit_cast(u32x2, x0)[0];
-        av[1] = __builtin_bit_cast(u32x2, x0)[1];
-        av[2] = __builtin_bit_cast(u32x2, x1)[0];
-        av[3] = __builtin_bit_cast(u32x2, x1)[1];
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), P.p[st], o[dt], 0, 0, 0);
-      }
-    }
+      for (int dt = 0; dt < 4; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_opnd(vb, st, dt), P.p[st], o[dt], 0, 0,
+                                                        0);
   };
 
   float m_ref = kNegInf;  // reference max (log2 domain) of row qrow, same on both halves
   float lpart = 0.f;      // this lane's half of the running sum
-  const float sl2 = p.scale_log2;
+  // |scale| * log2(e), kept away from zero so that masked (-inf) scores
+  // still give -inf; for |scale * q.k| far below 2^-24 * 32 the weights are
+  // the same as with the exact scale.
+  const float sl2 = fmaxf(p.scale_log2, 1e-30f);
   const int vis_last = p.causal ? p.offset + qrow : p.S_kv - 1;
-
-  // P = exp2(S*scale - ref) rounded to bf16; returns the fp32 sum of P over
-  // this lane's 32 keys.  Masked scores hold -inf and get weight 0.
-  auto exps = [&](const Tile16& T, PTile& P, float ref, bool masked) -> float {
-    const float negr = -ref;
-    float psum = 0.f;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int mt = st >> 1;
-      const int sp = st & 1;
-      u32x4 pw;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float x0 = T.s[mt][8 * sp + 2 * jj];
-        const float x1 = T.s[mt][8 * sp + 2 * jj + 1];
-        float e0 = fast_exp2(__builtin_fmaf(x0, sl2, negr));
-        float e1 = fast_exp2(__builtin_fmaf(x1, sl2, negr));
-        if (masked) {
-          e0 = x0 == kNegInf ? 0.f : e0;
-          e1 = x1 == kNegInf ? 0.f : e1;
-        }
-        pw[jj] = pack_bf16x2(e0, e1);
-        psum += e0 + e1;
-      }
-      P.p[st] = as_bf16x8(pw);
-    }
-    return psum;
-  };
 
   auto mask_tile = [&](Tile16& T, int tile) {
     const int kbase = tile * kBN;
@@ -252,82 +272,157 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       }
   };
 
-  auto lane_max = [&](const Tile16& T) {
+  auto half_max = [&](const f32x16& s) {
     float r = kNegInf;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) r = fmaxf(r, T.s[mt][i]);
+    for (int i = 0; i < 16; ++i) r = fmaxf(r, s[i]);
     return r;
   };
 
-  // Softmax of one tile.  The common case keeps the reference; the rare
-  // case (first tile, or a jump of the max) moves it with a full row max,
-  // rescales O and l, and recomputes P.
-  auto softmax = [&](Tile16& T, PTile& P, int tile, bool masked) {
-    if (masked) mask_tile(T, tile);
-    const float hmax = lane_max(T);
-    float psum = exps(T, P, m_ref, masked);
-    // Keep the speculative P in this block (next to the step's MFMAs)
-    // instead of letting the compiler sink it past the rare branch.
+  // Moves the reference to 32 below the row max of tile j when that max
+  // exceeds the reference by more than 64 (always on the first tile), and
+  // rescales everything kept relative to the old reference: O, l and the
+  // not yet applied P of tile j-1.
+  auto move_ref = [&](float hscaled, PTile& Pprev) {
+    const float rmax = wave_max_xor(hscaled, 32);
+    const float m_new = rmax > m_ref + kResetGap ? rmax - kRefBelow : m_ref;
+    const float corr = fast_exp2(m_ref - m_new);
+    lpart *= corr;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) asm volatile("" ::"v"(P.p[st]));
-    asm volatile("" ::"v"(psum));
-    const float hscaled = hmax == kNegInf ? kNegInf : hmax * sl2;
-    if (__any(hscaled > m_ref + kResetGap)) {
-      const float rmax = wave_max_xor(hscaled, 32);
-      const float m_new = rmax > m_ref + kResetGap ? rmax - kRefBelow : m_ref;
-      const float corr = fast_exp2(m_ref - m_new);
-      lpart *= corr;
+    for (int dt = 0; dt < 4; ++dt) o[dt] *= corr;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] *= corr;
-      m_ref = m_new;
-      psum = exps(T, P, m_ref, masked);
+    for (int st = 0; st < 4; ++st) {
+      const u32x4 w = __builtin_bit_cast(u32x4, Pprev.p[st]);
+      u32x4 r;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = __builtin_bit_cast(float, w[k] << 16) * corr;
+        const float hi = __builtin_bit_cast(float, w[k] & 0xffff0000u) * corr;
+        r[k] = pack_bf16x2(lo, hi);
+      }
+      Pprev.p[st] = as_bf16x8(r);
     }
-    lpart += psum;
+    m_ref = m_new;
   };
 
-  // Prologue: K tiles 0 and 1, V tile 0 in LDS; S of tile 0.
-  tile_load(sK[0], Kg, 0, false);
-  tile_load(sV[0], Vg, 0, true);
-  if (ntiles > 1) tile_load(sK[1], Kg, 1, false);
+  // One step's matrix work: the 32 MFMAs of P.V(j-1) and S(j+1) in one
+  // sequence, each MFMA's LDS operand read three MFMAs ahead, with the
+  // softmax of tile j (P = exp2(S*scale - ref), rounded to bf16; fp32 row
+  // sums) spread between them so that the matrix unit and the vector ALUs
+  // work at the same time.  Order: P.V key steps 0-1, S(j+1) rows 0-31,
+  // P.V key steps 2-3, S(j+1) rows 32-63; the exps of S(j) rows 0-31 go
+  // beside the first group (S(j+1) rows 0-31 then reuse their registers),
+  // those of rows 32-63 beside the second.
+  auto mma_step = [&](auto kbuf, auto vbuf, Tile16& T, const PTile& Pprev, PTile& Pcur) {
+    constexpr int kb = decltype(kbuf)::value;
+    constexpr int vb = decltype(vbuf)::value;
+    auto opnd = [&](int i) -> bf16x8 {
+      if (i < 8) return v_opnd(vb, i >> 2, i & 3);
+      if (i < 16) return k_opnd(kb, 0, i - 8);
+      if (i < 24) return v_opnd(vb, 2 + ((i - 16) >> 2), (i - 16) & 3);
+      return k_opnd(kb, 1, i - 24);
+    };
+    float negr = -m_ref;
+    // Anchor the softmax inputs here, so that no exponential is hoisted
+    // out of the sequence.
+    asm volatile("" : "+v"(negr));
+    float psum = 0.f;
+    u32x4 pw[4];
+    Tile16 Sn;
+    constexpr int kAhead = 3;   // operand reads in flight ahead of the MFMA
+    bf16x8 ring[kAhead + 1];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) ring[i] = opnd(i);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      // One slot per MFMA: the scheduler may not move work between slots.
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + kAhead < 32) ring[(i + kAhead) % (kAhead + 1)] = opnd(i + kAhead);
+      const bf16x8 a = ring[i % (kAhead + 1)];
+      if (i < 8) {
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Pprev.p[i >> 2], o[i & 3], 0, 0, 0);
+      } else if (i < 16) {
+        const f32x16 zero = {};
+        Sn.s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i - 8], i > 8 ? Sn.s[0] : zero,
+                                                          0, 0, 0);
+      } else if (i < 24) {
+        const int st = 2 + ((i - 16) >> 2);
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Pprev.p[st], o[i & 3], 0, 0, 0);
+      } else {
+        const f32x16 zero = {};
+        Sn.s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i - 24], i > 24 ? Sn.s[1] : zero,
+                                                          0, 0, 0);
+      }
+      // Softmax pair q of S(j) rows 32*mt .. (mt = 0 on slots 0-7, 1 on
+      // slots 8-15): keys 32*mt + 8*(q/4) + 4*h2 + 2*(q%4) + {0, 1}.
+      if (i < 16) {
+        const int mt = i >> 3, q = i & 7;
+        const float e0 = fast_exp2(__builtin_fmaf(T.s[mt][2 * q], sl2, negr));
+        const float e1 = fast_exp2(__builtin_fmaf(T.s[mt][2 * q + 1], sl2, negr));
+        psum += e0 + e1;
+        const unsigned w = pack_bf16x2(e0, e1);
+        // Keep this pair in this slot (not sunk towards its first use).
+        asm volatile("" ::"v"(w), "v"(psum));
+        pw[2 * mt + (q >> 2)][q & 3] = w;
+        if ((q & 3) == 3) Pcur.p[2 * mt + (q >> 2)] = as_bf16x8(pw[2 * mt + (q >> 2)]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    lpart += psum;
+    T = Sn;
+  };
+
+  // Prologue: K tiles 0-2 and V tile 0 in LDS, V buffer 3 (read as tile
+  // -1 by the first step, with P = 0) zeroed; S of tile 0.
+  tile_load(sK[0], Kg, 0, 0);
+  if (ntiles > 1) tile_load(sK[1], Kg, 1, 0);
+  if (ntiles > 2) tile_load(sK[2], Kg, 2, 0);
+  tile_load(sV[0], Vg, 0, 1);
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(sV[3]);
+    for (int i = t; i < kTileElems / 8; i += kThreads) z[i] = u32x4{0, 0, 0, 0};
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile loads landed
   __syncthreads();
-  Tile16 TA, TB;
+  Tile16 T;
   PTile PA, PB;
-  compute_s(TA, sK[0]);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) PB.p[st] = as_bf16x8(u32x4{0, 0, 0, 0});
+  compute_s(T, 0);
+  __syncthreads();                      // every wave has read K tile 0
 
-  // Step j: S of tile j+1 into `nxt`, P.V of tile j-1 from `pprev`, softmax
-  // of tile j (scores in `cur`) into `pcur`; K for j+2 and V for j+1 are
-  // loaded into the free LDS buffers.
-  auto step = [&](Tile16& cur, Tile16& nxt, PTile& pcur, const PTile& pprev, int j) {
-    if (j + 2 < ntiles) tile_load(sK[(j + 2) % kBufs], Kg, j + 2, false);
-    if (j + 1 < ntiles) tile_load(sV[(j + 1) % kBufs], Vg, j + 1, true);
-    const bool do_s = j + 1 < n_live;
-    const bool do_pv = j >= 1 && j - 1 < n_live;
-    const bool do_sm = j < n_live;
-    if (do_s && do_pv && do_sm && j < n_full) {
-      compute_s(nxt, sK[(j + 1) % kBufs]);
-      pv(pprev, sV[(j - 1) % kBufs]);
-      softmax(cur, pcur, j, false);
-    } else {
-      if (do_s) compute_s(nxt, sK[(j + 1) % kBufs]);
-      if (do_pv) pv(pprev, sV[(j - 1) % kBufs]);
-      if (do_sm) softmax(cur, pcur, j, j >= n_full);
-    }
+  // Step j: P.V of tile j-1, the softmax of tile j (scores in T) into
+  // `pcur`, and S of tile j+1 into T.  Tiles past the wave's last visible
+  // one are fully masked (P = 0), so every step runs the same sequence.
+  auto step = [&](auto kbuf, auto vbuf, PTile& pprev, PTile& pcur, int j) {
+    if (j >= n_full) mask_tile(T, j);
+    const float hmax = fmaxf(half_max(T.s[0]), half_max(T.s[1]));
+    const float hscaled = hmax * sl2;
+    if (__any(hscaled > m_ref + kResetGap)) move_ref(hscaled, pprev);
+    mma_step(kbuf, vbuf, T, pprev, pcur);
+  };
+  // Group of steps j, j+1 (j % 4 == 2*G): reads K tiles j+1, j+2 and V
+  // tiles j-1, j; first loads K tiles j+3, j+4 and V tiles j+1, j+2 into
+  // the buffers read by the previous group; one barrier at the end.
+  auto group = [&](auto gsel, int j) {
+    constexpr int G = decltype(gsel)::value;
+    if (j + 3 < ntiles) tile_load(sK[(2 * G + 3) % 4], Kg, j + 3, 0);
+    if (j + 4 < ntiles) tile_load(sK[(2 * G + 4) % 4], Kg, j + 4, 0);
+    if (j + 1 < ntiles) tile_load(sV[(2 * G + 1) % 4], Vg, j + 1, 1);
+    if (j + 2 < ntiles) tile_load(sV[(2 * G + 2) % 4], Vg, j + 2, 1);
+    step(Int<(2 * G + 1) % 4>(), Int<(2 * G + 3) % 4>(), PB, PA, j);
+    if (j + 1 < ntiles) step(Int<(2 * G + 2) % 4>(), Int<(2 * G) % 4>(), PA, PB, j + 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   };
-  int j = 0;
-  for (; j + 1 < ntiles; j += 2) {
-    step(TA, TB, PA, PB, j);
-    step(TB, TA, PB, PA, j + 1);
+  for (int j = 0; j < ntiles; j += 4) {
+    group(Int<0>(), j);
+    if (j + 2 < ntiles) group(Int<1>(), j + 2);
   }
-  if (j < ntiles) {
-    step(TA, TB, PA, PB, j);
-    if (n_live == ntiles) pv(PA, sV[j % kBufs]);   // P.V of the last tile
-  } else if (n_live == ntiles) {
-    pv(PB, sV[(j - 1) % kBufs]);
+  // P.V of the last tile: its P is in PA (even tile) or PB (odd tile).
+  {
+    const int last = ntiles - 1;
+    pv((last & 1) ? PB : PA, last & 3);
   }
 
   // Epilogue: O = O / l, rounded to bf16.  Lane holds, for d-tile dt and
