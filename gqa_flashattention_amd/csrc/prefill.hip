@@ -197,30 +197,43 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // Direct global -> LDS tile load: the waves split the 16 row groups of 4
   // rows; one 1 KiB instruction fills a group, lane l landing at physical
   // piece l%16 of row 4*group + l/16 and fetching the logical piece that
-  // belongs there.  Per lane, the byte offset inside a tile is fixed; rows
-  // past S_kv (last tile only) re-read the last valid row (finite data;
-  // those keys are masked and their V rows get weight 0).
+  // belongs there.  The loads go through a buffer resource that covers only
+  // the S_kv valid rows of this (sequence, KV head) from the tile on, so
+  // rows past S_kv read as zeros (no clamping, nothing outside the valid
+  // rows is touched); those keys are masked and their zero V rows get
+  // weight 0.  Tile indices past the last tile are clamped to it (the
+  // buffers they fill are never read).
   constexpr int kInsts = kBN / 4 / kWaves;   // 1 KiB (4-row) loads per wave
-  int ld_off[2][kInsts];                     // [K, V][instruction]
+  int ld_off[2][kInsts];                     // [K, V][instruction]: byte offset in a tile
 #pragma unroll
   for (int i = 0; i < kInsts; ++i) {
     const int row = 4 * (kInsts * wave + i) + (lane >> 4);
     ld_off[0][i] = row * (kD * 2) + 16 * k_swz(row, lane & 15);   // XOR is an involution
     ld_off[1][i] = row * (kD * 2) + 16 * v_swz(row, lane & 15);
   }
-  auto tile_load = [&](__bf16* buf, const __bf16* g, int tile, int kv) {
-    const char* base = reinterpret_cast<const char*>(g) + (size_t)tile * (kBN * kD * 2);
-    const bool tail = tile * kBN + kBN > p.S_kv;
+  const unsigned lds_k0 = lds_addr(&sK[0][0]), lds_v0 = lds_addr(&sV[0][0]);
+  // One load instruction (i) of tile `tile` of K (kv = 0) or V (kv = 1)
+  // into LDS buffer `buf`.  Issued as inline assembly: the compiler would
+  // otherwise make the next LDS read wait for it (it cannot tell the
+  // addresses apart).  All loads are waited for before each barrier.
+  auto tile_load_part = [&](int kv, int buf, int tile, int i) {
+    tile = min(tile, ntiles - 1);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(kv ? Vg : Kg) + (size_t)tile * (kBN * kD * 2);
+    u32x4 rsrc;
+    rsrc[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+    rsrc[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu);   // stride 0
+    rsrc[2] = __builtin_amdgcn_readfirstlane((unsigned)(p.S_kv - tile * kBN) * (kD * 2));
+    rsrc[3] = 0x00020000u;                     // raw buffer, 32-bit data format
+    const unsigned dst = __builtin_amdgcn_readfirstlane(
+        (kv ? lds_v0 : lds_k0) + buf * kTileBytes + 4 * (kInsts * wave + i) * kD * 2);
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(ld_off[kv][i]), "s"(rsrc), "s"(dst)
+                 : "memory");
+  };
+  auto tile_load = [&](int kv, int buf, int tile) {
 #pragma unroll
-    for (int i = 0; i < kInsts; ++i) {
-      const int row0 = 4 * (kInsts * wave + i);
-      int off = ld_off[kv][i];
-      if (tail) {
-        const int key = min(tile * kBN + row0 + (lane >> 4), p.S_kv - 1);
-        off = (key - tile * kBN) * (kD * 2) + (off & (kD * 2 - 1));
-      }
-      __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(buf + row0 * kD), 16, 0, 0);
-    }
+    for (int i = 0; i < kInsts; ++i) tile_load_part(kv, buf, tile, i);
   };
 
   // S^T of one tile from K buffer `kb`.
@@ -309,24 +322,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // sequence, each MFMA's LDS operand read three MFMAs ahead, with the
   // softmax of tile j (P = exp2(S*scale - ref), rounded to bf16; fp32 row
   // sums) spread between them so that the matrix unit and the vector ALUs
-  // work at the same time.  Order: P.V key steps 0-1, S(j+1) rows 0-31,
-  // P.V key steps 2-3, S(j+1) rows 32-63; the exps of S(j) rows 0-31 go
-  // beside the first group (S(j+1) rows 0-31 then reuse their registers),
-  // those of rows 32-63 beside the second.
-  auto mma_step = [&](auto kbuf, auto vbuf, Tile16& T, const PTile& Pprev, PTile& Pcur) {
+  // work at the same time.  Order: P.V key steps 0-1 beside the exps of
+  // S(j) rows 0-31; S(j+1) rows 0-31 (reusing those registers) beside the
+  // exps of rows 32-63; S(j+1) rows 32-63 beside the lane max of the new
+  // rows 0-31; P.V key steps 2-3 beside the lane max of the new rows
+  // 32-63.  Returns this lane's max over S(j+1) (unmasked).
+  // `ld` (when not null) lists the four tile loads of the group as
+  // {kv, buffer, tile} triples; their eight instructions are spread over
+  // the sequence (one every fourth MFMA) so that the load path is fed
+  // gradually instead of stalling the waves at the start of the group.
+  auto mma_step = [&](auto kbuf, auto vbuf, Tile16& T, const PTile& Pprev, PTile& Pcur,
+                      const int (*ld)[3]) {
     constexpr int kb = decltype(kbuf)::value;
     constexpr int vb = decltype(vbuf)::value;
     auto opnd = [&](int i) -> bf16x8 {
       if (i < 8) return v_opnd(vb, i >> 2, i & 3);
       if (i < 16) return k_opnd(kb, 0, i - 8);
-      if (i < 24) return v_opnd(vb, 2 + ((i - 16) >> 2), (i - 16) & 3);
-      return k_opnd(kb, 1, i - 24);
+      if (i < 24) return k_opnd(kb, 1, i - 16);
+      return v_opnd(vb, 2 + ((i - 24) >> 2), (i - 24) & 3);
     };
     float negr = -m_ref;
     // Anchor the softmax inputs here, so that no exponential is hoisted
     // out of the sequence.
     asm volatile("" : "+v"(negr));
     float psum = 0.f;
+    float nmax = kNegInf;
     u32x4 pw[4];
     Tile16 Sn;
     constexpr int kAhead = 3;   // operand reads in flight ahead of the MFMA
@@ -338,24 +358,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       // One slot per MFMA: the scheduler may not move work between slots.
       __builtin_amdgcn_sched_barrier(0);
       if (i + kAhead < 32) ring[(i + kAhead) % (kAhead + 1)] = opnd(i + kAhead);
+      if (ld != nullptr && (i & 3) == 2) {
+        const int* l = ld[i >> 3];
+        tile_load_part(l[0], l[1], l[2], (i >> 2) & 1);
+      }
       const bf16x8 a = ring[i % (kAhead + 1)];
+      const f32x16 zero = {};
       if (i < 8) {
         o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Pprev.p[i >> 2], o[i & 3], 0, 0, 0);
       } else if (i < 16) {
-        const f32x16 zero = {};
         Sn.s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i - 8], i > 8 ? Sn.s[0] : zero,
                                                           0, 0, 0);
       } else if (i < 24) {
-        const int st = 2 + ((i - 16) >> 2);
-        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Pprev.p[st], o[i & 3], 0, 0, 0);
-      } else {
-        const f32x16 zero = {};
-        Sn.s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i - 24], i > 24 ? Sn.s[1] : zero,
+        Sn.s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i - 16], i > 16 ? Sn.s[1] : zero,
                                                           0, 0, 0);
+      } else {
+        const int st = 2 + ((i - 24) >> 2);
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Pprev.p[st], o[i & 3], 0, 0, 0);
       }
-      // Softmax pair q of S(j) rows 32*mt .. (mt = 0 on slots 0-7, 1 on
-      // slots 8-15): keys 32*mt + 8*(q/4) + 4*h2 + 2*(q%4) + {0, 1}.
       if (i < 16) {
+        // Softmax pair q of S(j) rows 32*mt..: keys 32*mt + 8*(q/4) + 4*h2
+        // + 2*(q%4) + {0, 1}.
         const int mt = i >> 3, q = i & 7;
         const float e0 = fast_exp2(__builtin_fmaf(T.s[mt][2 * q], sl2, negr));
         const float e1 = fast_exp2(__builtin_fmaf(T.s[mt][2 * q + 1], sl2, negr));
@@ -365,19 +388,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
         asm volatile("" ::"v"(w), "v"(psum));
         pw[2 * mt + (q >> 2)][q & 3] = w;
         if ((q & 3) == 3) Pcur.p[2 * mt + (q >> 2)] = as_bf16x8(pw[2 * mt + (q >> 2)]);
+      } else {
+        // Lane max of S(j+1): rows 0-31 on slots 16-23, rows 32-63 on
+        // slots 24-31 (each half is complete by then).
+        const int mt = (i - 16) >> 3, q = i & 7;
+        nmax = fmaxf(nmax, fmaxf(Sn.s[mt][2 * q], Sn.s[mt][2 * q + 1]));
+        asm volatile("" ::"v"(nmax));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     lpart += psum;
     T = Sn;
+    return nmax;
   };
 
   // Prologue: K tiles 0-2 and V tile 0 in LDS, V buffer 3 (read as tile
   // -1 by the first step, with P = 0) zeroed; S of tile 0.
-  tile_load(sK[0], Kg, 0, 0);
-  if (ntiles > 1) tile_load(sK[1], Kg, 1, 0);
-  if (ntiles > 2) tile_load(sK[2], Kg, 2, 0);
-  tile_load(sV[0], Vg, 0, 1);
+  tile_load(0, 0, 0);
+  if (ntiles > 1) tile_load(0, 1, 1);
+  if (ntiles > 2) tile_load(0, 2, 2);
+  tile_load(1, 0, 0);
   {
     u32x4* z = reinterpret_cast<u32x4*>(sV[3]);
     for (int i = t; i < kTileElems / 8; i += kThreads) z[i] = u32x4{0, 0, 0, 0};
@@ -389,29 +419,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
 #pragma unroll
   for (int st = 0; st < 4; ++st) PB.p[st] = as_bf16x8(u32x4{0, 0, 0, 0});
   compute_s(T, 0);
+  float tmax = fmaxf(half_max(T.s[0]), half_max(T.s[1]));   // lane max of the scores in T
   __syncthreads();                      // every wave has read K tile 0
 
   // Step j: P.V of tile j-1, the softmax of tile j (scores in T) into
   // `pcur`, and S of tile j+1 into T.  Tiles past the wave's last visible
   // one are fully masked (P = 0), so every step runs the same sequence.
-  auto step = [&](auto kbuf, auto vbuf, PTile& pprev, PTile& pcur, int j) {
-    if (j >= n_full) mask_tile(T, j);
-    const float hmax = fmaxf(half_max(T.s[0]), half_max(T.s[1]));
-    const float hscaled = hmax * sl2;
+  auto step = [&](auto kbuf, auto vbuf, PTile& pprev, PTile& pcur, int j, const int (*ld)[3]) {
+    if (j >= n_full) {   // masked tile: the carried max is recomputed
+      mask_tile(T, j);
+      tmax = fmaxf(half_max(T.s[0]), half_max(T.s[1]));
+    }
+    const float hscaled = tmax * sl2;
     if (__any(hscaled > m_ref + kResetGap)) move_ref(hscaled, pprev);
-    mma_step(kbuf, vbuf, T, pprev, pcur);
+    tmax = mma_step(kbuf, vbuf, T, pprev, pcur, ld);
   };
   // Group of steps j, j+1 (j % 4 == 2*G): reads K tiles j+1, j+2 and V
   // tiles j-1, j; first loads K tiles j+3, j+4 and V tiles j+1, j+2 into
   // the buffers read by the previous group; one barrier at the end.
   auto group = [&](auto gsel, int j) {
     constexpr int G = decltype(gsel)::value;
-    if (j + 3 < ntiles) tile_load(sK[(2 * G + 3) % 4], Kg, j + 3, 0);
-    if (j + 4 < ntiles) tile_load(sK[(2 * G + 4) % 4], Kg, j + 4, 0);
-    if (j + 1 < ntiles) tile_load(sV[(2 * G + 1) % 4], Vg, j + 1, 1);
-    if (j + 2 < ntiles) tile_load(sV[(2 * G + 2) % 4], Vg, j + 2, 1);
-    step(Int<(2 * G + 1) % 4>(), Int<(2 * G + 3) % 4>(), PB, PA, j);
-    if (j + 1 < ntiles) step(Int<(2 * G + 2) % 4>(), Int<(2 * G) % 4>(), PA, PB, j + 1);
+    const int ld[4][3] = {{0, (2 * G + 3) % 4, j + 3},
+                          {0, (2 * G + 4) % 4, j + 4},
+                          {1, (2 * G + 1) % 4, j + 1},
+                          {1, (2 * G + 2) % 4, j + 2}};
+    step(Int<(2 * G + 1) % 4>(), Int<(2 * G + 3) % 4>(), PB, PA, j, ld);
+    if (j + 1 < ntiles) step(Int<(2 * G + 2) % 4>(), Int<(2 * G) % 4>(), PA, PB, j + 1, nullptr);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   };
