@@ -61,6 +61,7 @@ constexpr int kTileElems = kBN * kD; // 16 KiB of bf16 per tile, unpadded
 constexpr int kBufs = 4;              // K and V tile rings (tile t in buffer t % 4)
 
 constexpr float kResetGap = 64.f;    // log2 units
+constexpr float kPsumLimit = 18446744073709551616.f;   // 2^64 = exp2(kResetGap)
 constexpr float kRefBelow = 32.f;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -292,30 +293,38 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     return r;
   };
 
-  // Moves the reference to 32 below the row max of tile j when that max
-  // exceeds the reference by more than 64 (always on the first tile), and
-  // rescales everything kept relative to the old reference: O, l and the
-  // not yet applied P of tile j-1.
-  auto move_ref = [&](float hscaled, PTile& Pprev) {
+  // Moves the reference to 32 below the row max when that max (log2 units,
+  // `hscaled` per lane) exceeds the reference by more than 64, rescaling O
+  // and l, which are kept relative to the reference.
+  auto move_ref = [&](float hscaled) {
     const float rmax = wave_max_xor(hscaled, 32);
     const float m_new = rmax > m_ref + kResetGap ? rmax - kRefBelow : m_ref;
     const float corr = fast_exp2(m_ref - m_new);
     lpart *= corr;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] *= corr;
+    m_ref = m_new;
+  };
+
+  // P = exp2(S*scale - ref) rounded to bf16; returns the fp32 sum of P over
+  // this lane's 32 keys (masked scores are -inf and give 0).
+  auto exps = [&](const Tile16& T, PTile& P) -> float {
+    const float negr = -m_ref;
+    float psum = 0.f;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const u32x4 w = __builtin_bit_cast(u32x4, Pprev.p[st]);
-      u32x4 r;
+      u32x4 pw;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float lo = __builtin_bit_cast(float, w[k] << 16) * corr;
-        const float hi = __builtin_bit_cast(float, w[k] & 0xffff0000u) * corr;
-        r[k] = pack_bf16x2(lo, hi);
+      for (int jj = 0; jj < 4; ++jj) {
+        const float e0 = fast_exp2(__builtin_fmaf(T.s[st >> 1][8 * (st & 1) + 2 * jj], sl2, negr));
+        const float e1 =
+            fast_exp2(__builtin_fmaf(T.s[st >> 1][8 * (st & 1) + 2 * jj + 1], sl2, negr));
+        psum += e0 + e1;
+        pw[jj] = pack_bf16x2(e0, e1);
       }
-      Pprev.p[st] = as_bf16x8(r);
+      P.p[st] = as_bf16x8(pw);
     }
-    m_ref = m_new;
+    return psum;
   };
 
   // One step's matrix work: the 32 MFMAs of P.V(j-1) and S(j+1) in one
@@ -324,13 +333,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // sums) spread between them so that the matrix unit and the vector ALUs
   // work at the same time.  Order: P.V key steps 0-1 beside the exps of
   // S(j) rows 0-31; S(j+1) rows 0-31 (reusing those registers) beside the
-  // exps of rows 32-63; S(j+1) rows 32-63 beside the lane max of the new
-  // rows 0-31; P.V key steps 2-3 beside the lane max of the new rows
-  // 32-63.  Returns this lane's max over S(j+1) (unmasked).
-  // `ld` (when not null) lists the four tile loads of the group as
-  // {kv, buffer, tile} triples; their eight instructions are spread over
-  // the sequence (one every fourth MFMA) so that the load path is fed
-  // gradually instead of stalling the waves at the start of the group.
+  // exps of rows 32-63; S(j+1) rows 32-63; P.V key steps 2-3.  Returns
+  // this lane's fp32 sum of P(j).
+  // `ld` (when not null) lists two tile loads as {kv, buffer, tile}
+  // triples; their four instructions are spread over the sequence (one
+  // every eighth MFMA) so that the load path is fed gradually instead of
+  // stalling the waves at the start of the group.
   auto mma_step = [&](auto kbuf, auto vbuf, Tile16& T, const PTile& Pprev, PTile& Pcur,
                       const int (*ld)[3]) {
     constexpr int kb = decltype(kbuf)::value;
@@ -346,7 +354,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     // out of the sequence.
     asm volatile("" : "+v"(negr));
     float psum = 0.f;
-    float nmax = kNegInf;
     u32x4 pw[4];
     Tile16 Sn;
     constexpr int kAhead = 3;   // operand reads in flight ahead of the MFMA
@@ -358,9 +365,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       // One slot per MFMA: the scheduler may not move work between slots.
       __builtin_amdgcn_sched_barrier(0);
       if (i + kAhead < 32) ring[(i + kAhead) % (kAhead + 1)] = opnd(i + kAhead);
-      if (ld != nullptr && (i & 3) == 2) {
-        const int* l = ld[i >> 3];
-        tile_load_part(l[0], l[1], l[2], (i >> 2) & 1);
+      if (ld != nullptr && (i & 7) == 2) {
+        const int* l = ld[i >> 4];
+        tile_load_part(l[0], l[1], l[2], (i >> 3) & 1);
       }
       const bf16x8 a = ring[i % (kAhead + 1)];
       const f32x16 zero = {};
@@ -388,18 +395,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
         asm volatile("" ::"v"(w), "v"(psum));
         pw[2 * mt + (q >> 2)][q & 3] = w;
         if ((q & 3) == 3) Pcur.p[2 * mt + (q >> 2)] = as_bf16x8(pw[2 * mt + (q >> 2)]);
-      } else {
-        // Lane max of S(j+1): rows 0-31 on slots 16-23, rows 32-63 on
-        // slots 24-31 (each half is complete by then).
-        const int mt = (i - 16) >> 3, q = i & 7;
-        nmax = fmaxf(nmax, fmaxf(Sn.s[mt][2 * q], Sn.s[mt][2 * q + 1]));
-        asm volatile("" ::"v"(nmax));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    lpart += psum;
     T = Sn;
-    return nmax;
+    return psum;
   };
 
   // Prologue: K tiles 0-2 and V tile 0 in LDS, V buffer 3 (read as tile
@@ -419,32 +419,45 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
 #pragma unroll
   for (int st = 0; st < 4; ++st) PB.p[st] = as_bf16x8(u32x4{0, 0, 0, 0});
   compute_s(T, 0);
-  float tmax = fmaxf(half_max(T.s[0]), half_max(T.s[1]));   // lane max of the scores in T
   __syncthreads();                      // every wave has read K tile 0
 
   // Step j: P.V of tile j-1, the softmax of tile j (scores in T) into
   // `pcur`, and S of tile j+1 into T.  Tiles past the wave's last visible
   // one are fully masked (P = 0), so every step runs the same sequence.
+  // The softmax uses the current reference; if any weight exceeds 2^64
+  // (some score is more than 64 above the reference: always on the first
+  // tile, rarely later) the lane sum shows it, and the tile's scores are
+  // recomputed from K (still in LDS), the reference moved and P redone.
   auto step = [&](auto kbuf, auto vbuf, PTile& pprev, PTile& pcur, int j, const int (*ld)[3]) {
-    if (j >= n_full) {   // masked tile: the carried max is recomputed
-      mask_tile(T, j);
-      tmax = fmaxf(half_max(T.s[0]), half_max(T.s[1]));
+    constexpr int kb = decltype(kbuf)::value;   // K buffer of tile j+1
+    if (j >= n_full) mask_tile(T, j);
+    float psum = mma_step(kbuf, vbuf, T, pprev, pcur, ld);
+    if (__any(!(psum <= kPsumLimit))) {
+      Tile16 Tj;
+      compute_s(Tj, (kb + 3) % 4);            // K buffer of tile j
+      if (j >= n_full) mask_tile(Tj, j);
+      const float hmax = fmaxf(half_max(Tj.s[0]), half_max(Tj.s[1]));
+      move_ref(hmax * sl2);
+      psum = exps(Tj, pcur);
     }
-    const float hscaled = tmax * sl2;
-    if (__any(hscaled > m_ref + kResetGap)) move_ref(hscaled, pprev);
-    tmax = mma_step(kbuf, vbuf, T, pprev, pcur, ld);
+    lpart += psum;
   };
   // Group of steps j, j+1 (j % 4 == 2*G): reads K tiles j+1, j+2 and V
-  // tiles j-1, j; first loads K tiles j+3, j+4 and V tiles j+1, j+2 into
-  // the buffers read by the previous group; one barrier at the end.
+  // tiles j-1, j; loads V tiles j+1, j+2 during step j and K tiles j+3,
+  // j+4 during step j+1 (K tile j stays in LDS through step j, K tile j+1
+  // through step j+1), all into buffers the previous group read; one
+  // barrier at the end.
   auto group = [&](auto gsel, int j) {
     constexpr int G = decltype(gsel)::value;
-    const int ld[4][3] = {{0, (2 * G + 3) % 4, j + 3},
-                          {0, (2 * G + 4) % 4, j + 4},
-                          {1, (2 * G + 1) % 4, j + 1},
-                          {1, (2 * G + 2) % 4, j + 2}};
-    step(Int<(2 * G + 1) % 4>(), Int<(2 * G + 3) % 4>(), PB, PA, j, ld);
-    if (j + 1 < ntiles) step(Int<(2 * G + 2) % 4>(), Int<(2 * G) % 4>(), PA, PB, j + 1, nullptr);
+    const int ldv[2][3] = {{1, (2 * G + 1) % 4, j + 1}, {1, (2 * G + 2) % 4, j + 2}};
+    const int ldk[2][3] = {{0, (2 * G + 3) % 4, j + 3}, {0, (2 * G + 4) % 4, j + 4}};
+    step(Int<(2 * G + 1) % 4>(), Int<(2 * G + 3) % 4>(), PB, PA, j, ldv);
+    if (j + 1 < ntiles) {
+      step(Int<(2 * G + 2) % 4>(), Int<(2 * G) % 4>(), PA, PB, j + 1, ldk);
+    } else {
+      tile_load(0, (2 * G + 3) % 4, j + 3);
+      tile_load(0, (2 * G + 4) % 4, j + 4);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   };

@@ -189,3 +189,19 @@ def test_decode_phases_equal_one_call():
               return_lse=True, out=two, lse=l2, workspace=ws, phase="combine")
     torch.cuda.synchronize()
     assert torch.equal(one, two) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("chunk", [0, 128])
+def test_decode_max_jump(chunk):
+    """Keys of one later stretch scaled by 40 (and a few more by 25): the
+    running max jumps inside a split and between splits; every element
+    against the oracle."""
+    w = inputs.Workload("t", "decode", B=2, H_q=16, H_kv=2, d=128, dtype="bf16",
+                        lens=(5000, 3100), kv_cap=5000)
+    banner("decode_max_jump", chunk)
+    x = inputs.make_decode(w, device=DEV, seed=17)
+    x["k"][:, :, 3000:3100] *= 40.0
+    x["k"][:, :, 4500:4510] *= 25.0
+    o, lse = _run(x, w, chunk)
+    ref_o, ref_lse = _oracle(x, w)
+    _check(o, lse, ref_o, ref_lse, w, f"max jump chunk={chunk}")

@@ -149,3 +149,23 @@ def test_prefill_scale_sign_and_zero(scale):
                             causal_offset=110)
     check_bf16(np32(o[0]), ro[0], f"scale {scale}")
     check_lse(np32(lse), rl, f"scale {scale}", LSE_ATOL_BF16)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_max_jump_moves_reference(causal):
+    """Keys of one later tile scaled by 40: their scores jump far above the
+    running reference, so the reference must move mid-sequence (O, l and the
+    pending P rescaled).  Every element against the oracle."""
+    w = inputs.Workload("t", "prefill", B=1, H_q=16, H_kv=2, d=128, dtype="bf16", S_q=200,
+                        S_kv=700, causal=causal, offset=500 if causal else 0)
+    banner("prefill_max_jump", causal)
+    x = inputs.make_prefill(w, device=DEV, seed=24)
+    x["k"][:, :, 320:384] *= 40.0          # tile 5
+    x["k"][:, :, 600:610] *= 25.0          # a smaller second jump inside tile 9
+    o, lse = gq.prefill(x["q"], x["k"], x["v"], S_kv=w.S_kv, causal=causal,
+                        causal_offset=w.offset, scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill(np32(x["q"]), np32(x["k"]), np32(x["v"]), w.S_kv, w.scale,
+                            causal=causal, causal_offset=w.offset)
+    check_bf16(np32(o[0]), ro[0], f"max jump causal={causal}")
+    check_lse(np32(lse), rl, f"max jump causal={causal}", LSE_ATOL_BF16)
