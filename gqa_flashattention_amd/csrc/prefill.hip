@@ -227,7 +227,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     rsrc[3] = 0x00020000u;                     // raw buffer, 32-bit data format
     const unsigned dst = __builtin_amdgcn_readfirstlane(
         (kv ? lds_v0 : lds_k0) + buf * kTileBytes + 4 * (kInsts * wave + i) * kD * 2);
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    // Wait states inside the statement (the compiler's hazard checks do not
+    // look into inline assembly): the descriptor and M0 value were just
+    // written by VALU (v_readfirstlane), and an LDS DMA may not follow an
+    // M0 write directly.
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
                  : "v"(ld_off[kv][i]), "s"(rsrc), "s"(dst)
                  : "memory");
