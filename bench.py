@@ -6,15 +6,18 @@ One step = one pass over both entry points on one batch of synthetic input:
   * prefill: causal, S_q = S_kv = 8192, same geometry, bf16.
 
 ``value`` is decode KV throughput in GB/s: algorithmic bytes (K and V of the
-valid keys, plus Q and O) per decode call divided by the call's time, with
-inputs resident in HBM.  The decode K/V cache rotates over ``--kv-copies``
-distinct copies (default 4 x 128 MiB) so the 256 MB Infinity Cache cannot
-serve it from one call to the next.  The prefill figure (TFLOP/s over the
-exact causal visible-pair FLOPs) is reported in the ``prefill`` object.
+valid keys, plus Q and O) per decode call divided by the time per call of K
+back-to-back gqa_attn_decode calls, with inputs resident in HBM.  The decode
+K/V cache rotates over ``--kv-copies`` distinct copies (default 4 x 128 MiB)
+so the 256 MB Infinity Cache cannot serve it from one call to the next.  The
+prefill figure (TFLOP/s over the exact causal visible-pair FLOPs) is
+reported in the ``prefill`` object.
 
-Timing uses HIP events on the stream the kernels run on, around every call
-of the timed region; warm-up calls are untimed.  ``cpu_baseline`` times the
-fp64 oracle on the host cores on a bounded sample of the same workload.
+Timing uses HIP events on the stream the kernels run on: around every call
+of the K timed steps (decode + prefill), and around the K back-to-back
+decode calls and K split-kernel launches that follow; warm-up calls are
+untimed.  ``cpu_baseline`` times the fp64 oracle on the host cores on a
+bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -202,12 +205,18 @@ def main():
             prefill_call()
     torch.cuda.synchronize()
 
-    # Timed region.  (1) K steps: one gqa_attn_decode call and one prefill
-    # call each, HIP events around every call.  (2) The decode split kernel
-    # alone (gqa_attn_decode_partial), K back-to-back launches between two
-    # events, for its per-launch duration (the roofline kernel).
+    # Timed region.
+    #  (1) K steps: one gqa_attn_decode call and one prefill call each, HIP
+    #      events around every call (ms_per_step; the prefill figure).
+    #  (2) K gqa_attn_decode calls back to back (rotating K/V copies) between
+    #      two events: the decode throughput, `value`.  Per-call events would
+    #      add their own overhead to a ~30 us call.
+    #  (3) K launches of the decode split kernel alone
+    #      (gqa_attn_decode_partial) between two events: its per-launch
+    #      duration, for the roofline.
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    kd = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     kp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -220,6 +229,10 @@ def main():
             prefill_call()
         ev[i][2].record(stream)
     if do_dec:
+        kd[0].record(stream)
+        for i in range(K):
+            decode_call(i)
+        kd[1].record(stream)
         kp[0].record(stream)
         for i in range(K):
             decode_call(i, "partial")
@@ -229,6 +242,7 @@ def main():
     dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
     pre_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
     step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
+    dec_b2b_us = kd[0].elapsed_time(kd[1]) * 1e3 / K if do_dec else None
     part_us = kp[0].elapsed_time(kp[1]) * 1e3 / K if do_dec else None
     mean = lambda a: sum(a) / len(a)
     median = lambda a: sorted(a)[len(a) // 2]
@@ -256,13 +270,15 @@ def main():
         "wall_s_timed_region": round(wall, 4),
     }
     if do_dec:
-        t_s = mean(dec_ms) / 1e3
+        t_s = dec_b2b_us / 1e6
         gbs = wd.decode_bytes() / t_s / 1e9
         # Split kernel's algorithmic bytes: K and V of the valid keys plus Q.
         part_bytes = wd.kv_bytes() + wd.B * wd.H_q * wd.d * wd.elem_bytes
         part_gbs = part_bytes / (part_us / 1e6) / 1e9
         out["value"] = round(gbs, 2)
-        out["decode"] = {"ms_mean": round(mean(dec_ms), 6), "ms_median": round(median(dec_ms), 6),
+        out["decode"] = {"us_per_call_back_to_back": round(dec_b2b_us, 3),
+                         "ms_mean_in_step": round(mean(dec_ms), 6),
+                         "ms_median_in_step": round(median(dec_ms), 6),
                          "GB_s": round(gbs, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                          "bytes_per_call": wd.decode_bytes(),
                          "partial_kernel_us_mean": round(part_us, 3)}
