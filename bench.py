@@ -73,9 +73,10 @@ def calibrate_copy():
           flush=True)
 
 
-def traffic_from_profiles(kernel: str):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source; otherwise None."""
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary, if it was taken on the current kernel source; otherwise
+    None."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_decode_llama70b_32k_prefill_causal_8k.md")
     if not os.path.exists(path):
         return None
@@ -86,7 +87,7 @@ def traffic_from_profiles(kernel: str):
         return None
     table = json.loads(m.group(1))
     ent = table.get(kernel)
-    if not ent:
+    if not ent or ent.get("workload") != workload:
         return None
     src = os.path.join(ROOT, "gqa_flashattention_amd", "csrc", ent["source"])
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
@@ -170,6 +171,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     wd = inputs.WORKLOADS[args.decode_workload]
+    dec_dtype = gq.DTYPE_F32 if wd.dtype == "f32" else gq.DTYPE_BF16
     wp = inputs.WORKLOADS[args.prefill_workload]
     do_dec = args.only in ("decode", "both")
     do_pre = args.only in ("prefill", "both")
@@ -179,10 +181,10 @@ def main():
         copies = [inputs.make_decode(wd, device=dev, seed=inputs.SEEDS[wd.name] + 100 * i)
                   for i in range(max(1, args.kv_copies))]
         need = gq.decode_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.max_kv_len, args.chunk,
-                                         gq.DTYPE_BF16)
+                                         dec_dtype)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         o_dec = torch.empty_like(copies[0]["q"])
-        chunk = gq.decode_split_tokens(wd.B, wd.H_kv, wd.max_kv_len, args.chunk, gq.DTYPE_BF16)
+        chunk = gq.decode_split_tokens(wd.B, wd.H_kv, wd.max_kv_len, args.chunk, dec_dtype)
     if do_pre:
         xp = inputs.make_prefill(wp, device=dev)
         o_pre = torch.empty_like(xp["q"])
@@ -258,9 +260,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wd.dtype if args.only == "decode" else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{wd.name} + {wp.name}",
+        "config": {"workload": " + ".join(n for n, on in ((wd.name, do_dec), (wp.name, do_pre)) if on),
                    "decode": {"B": wd.B, "H_q": wd.H_q, "H_kv": wd.H_kv, "d": wd.d,
                               "kv_lens": list(wd.lens), "kv_copies": len(copies) if do_dec else 0,
                               "keys_per_split": chunk if do_dec else None},
@@ -282,10 +284,10 @@ def main():
                          "GB_s": round(gbs, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                          "bytes_per_call": wd.decode_bytes(),
                          "partial_kernel_us_mean": round(part_us, 3)}
-        out["roofline"] = {"bound": "hbm", "kernel": "decode_partial_bf16_kernel",
+        out["roofline"] = {"bound": "hbm", "kernel": f"decode_partial_{wd.dtype}_kernel",
                            "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(part_gbs / HBM_PEAK_GBS, 4),
-                           "traffic": traffic_from_profiles("decode_partial"),
+                           "traffic": traffic_from_profiles("decode_partial", wd.name),
                            "algorithmic_bytes_per_launch": part_bytes,
                            "launch_us_mean": round(part_us, 3)}
     if do_pre:
@@ -297,8 +299,13 @@ def main():
                           "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel",
                                        "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                                       "traffic": traffic_from_profiles("prefill"),
+                                       "traffic": traffic_from_profiles("prefill", wp.name),
                                        "launch_us_mean": round(mean(pre_ms) * 1e3, 3)}}
+
+    if not do_dec:   # prefill-only run: its throughput is the value
+        out["value"] = out["prefill"]["value"]
+        out["unit"] = "TFLOP/s"
+        out["roofline"] = out["prefill"]["roofline"]
 
     if not args.no_cpu_baseline:
         import numpy as np  # noqa: F401

@@ -12,7 +12,7 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kMaxG = 16;          // query heads per KV head the decode MFMA tile holds
-constexpr int kF32Chunk = 256;     // keys per split of the fp32 decode path
+constexpr int kF32Chunk = 64;      // keys per split of the fp32 decode path
 constexpr int kBf16ChunkQuantum = 128;  // 4 waves x 32-key blocks
 constexpr size_t kWsAlign = 256;
 

@@ -251,61 +251,94 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
   }
 }
 
-// fp32 decode partial: one workgroup of 256 threads per 256-key split.  A
-// one-shot partial over the split (score -> max/sum -> P.V, the "fits in
-// scratch" shape of §5.2), all in fp32 on the vector ALUs.
+// fp32 decode partial: one workgroup of 256 threads per 64-key split.  The
+// split's K and V rows (32 KiB each) and the group's Q rows are staged in
+// LDS with all loads in flight at once; then scores, the split's max and
+// sum, and P.V are computed from LDS on the vector ALUs in fp32 (a one-shot
+// partial over the split, the "fits in scratch" shape of §5.2).
+constexpr int kF32Chunk = 64;
+
 __global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p) {
-  constexpr int kChunk = 256;
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int L = p.kv_lens[b];
-  const int start = split * kChunk;
+  const int start = split * kF32Chunk;
   if (start >= L) return;
-  const int cnt = min(kChunk, L - start);
+  const int cnt = min(kF32Chunk, L - start);
   const int t = threadIdx.x;
   const float* q = static_cast<const float*>(p.q) + ((size_t)b * p.H_q + (size_t)kvh * p.G) * kD;
   const float* kbase = static_cast<const float*>(p.k) + (((size_t)b * p.H_kv + kvh) * p.kv_cap + start) * kD;
   const float* vbase = static_cast<const float*>(p.v) + (((size_t)b * p.H_kv + kvh) * p.kv_cap + start) * kD;
 
-  __shared__ float sq[16][kD];
-  __shared__ float ss[16][kChunk];
+  __shared__ __attribute__((aligned(16))) float sq[16][kD];
+  __shared__ float sk[kF32Chunk][kD + 1];   // +1: a wave reading one column of 64 rows hits 64 banks
+  __shared__ __attribute__((aligned(16))) float sv[kF32Chunk][kD];
+  __shared__ float ss[16][kF32Chunk];
   __shared__ float sm[16], sl[16];
-  for (int e = t; e < p.G * kD; e += 256) sq[e >> 7][e & (kD - 1)] = q[e];
-  __syncthreads();
 
-  // Scores: thread t owns key start + t.
-  if (t < cnt) {
-    float acc[16];
+  // Stage Q, K and V.  Rows past the valid length re-read the last valid
+  // row; their scores are masked and their V rows are stored as zeros, so
+  // the zero weights never meet padding.  Every global load is
+  // issued before the first LDS store, so the staging costs one memory
+  // round trip.
+  constexpr int kTileF4 = kF32Chunk * kD / 4 / 256;   // float4 per thread per tile
+  f32x4 qv[2], kv[kTileF4], vv[kTileF4];
 #pragma unroll
-    for (int n = 0; n < 16; ++n) acc[n] = 0.f;
-    const float* krow = kbase + (size_t)t * kD;
-    for (int d4 = 0; d4 < kD; d4 += 4) {
-      const f32x4 kv4 = *reinterpret_cast<const f32x4*>(krow + d4);
+  for (int i = 0; i < 2; ++i) {
+    const int e4 = t + 256 * i;
+    qv[i] = 4 * e4 < p.G * kD ? *reinterpret_cast<const f32x4*>(q + 4 * e4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
-      for (int n = 0; n < 16; ++n) {
-        if (n < p.G)
-          acc[n] += sq[n][d4] * kv4[0] + sq[n][d4 + 1] * kv4[1] + sq[n][d4 + 2] * kv4[2] + sq[n][d4 + 3] * kv4[3];
-      }
-    }
-    for (int n = 0; n < p.G; ++n) ss[n][t] = acc[n] * p.scale_log2;
-  } else {
-    for (int n = 0; n < p.G; ++n) ss[n][t] = kNegInf;
+  for (int i = 0; i < kTileF4; ++i) {
+    const int e4 = t + 256 * i;          // float4 index within the tile
+    const int row = min(e4 >> 5, cnt - 1), c4 = (e4 & 31) * 4;   // rows past cnt re-read the last
+    kv[i] = *reinterpret_cast<const f32x4*>(kbase + (size_t)row * kD + c4);
+    vv[i] = *reinterpret_cast<const f32x4*>(vbase + (size_t)row * kD + c4);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e4 = t + 256 * i;
+    if (4 * e4 < p.G * kD) *reinterpret_cast<f32x4*>(&sq[0][0] + 4 * e4) = qv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kTileF4; ++i) {
+    const int e4 = t + 256 * i;
+    const int row = e4 >> 5, c4 = (e4 & 31) * 4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sk[row][c4 + c] = kv[i][c];
+    *reinterpret_cast<f32x4*>(&sv[row][c4]) = row < cnt ? vv[i] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
 
-  // Row max and sum: wave w handles queries w, w+4, ...
+  // Scores: thread t -> key j = t % 64, queries t/64, t/64 + 4, ...
+  {
+    const int j = t & (kF32Chunk - 1);
+    const int n0 = t >> 6;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+    for (int d = 0; d < kD; ++d) {
+      const float kd = sk[j][d];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = __builtin_fmaf(sq[n0 + 4 * u][d], kd, acc[u]);   // rows >= G unused
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int n = n0 + 4 * u;
+      if (n < p.G) ss[n][j] = j < cnt ? acc[u] * p.scale_log2 : kNegInf;
+    }
+  }
+  __syncthreads();
+
+  // Max and sum of the split: wave w handles queries w, w + 4, ...; lane =
+  // key.
   const int wave = t >> 6, lane = t & 63;
   for (int n = wave; n < p.G; n += 4) {
-    float mx = kNegInf;
-    for (int j = lane; j < kChunk; j += 64) mx = fmaxf(mx, ss[n][j]);
+    float mx = ss[n][lane];
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    float sum = 0.f;
-    for (int j = lane; j < kChunk; j += 64) {
-      const float e = fast_exp2(ss[n][j] - mx);
-      ss[n][j] = e;
-      sum += e;
-    }
+    const float e = fast_exp2(ss[n][lane] - mx);   // the split has >= 1 valid key
+    ss[n][lane] = e;
+    float sum = e;
     for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
     if (lane == 0) {
       sm[n] = mx;
@@ -314,17 +347,28 @@ __global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p)
   }
   __syncthreads();
 
-  // O = P . V: thread t -> column d = t % 128, queries t/128, t/128 + 2, ...
+  // O = P . V: thread t -> column d = t % 128, queries t/128 + 2u (all of
+  // them in one pass over the keys, one accumulator each).
   const int dd = t & (kD - 1);
+  const int n0 = t >> 7;
   const size_t part0 = ((size_t)b * p.H_q + (size_t)kvh * p.G) * p.n_split_max + split;
-  for (int n = t >> 7; n < p.G; n += 2) {
-    float acc = 0.f;
-    for (int j = 0; j < cnt; ++j) acc += ss[n][j] * vbase[(size_t)j * kD + dd];
-    const size_t part = part0 + (size_t)n * p.n_split_max;
-    p.ws_o[part * kD + dd] = acc;
-    if (dd == 0) {
-      p.ws_ml[2 * part] = sm[n];
-      p.ws_ml[2 * part + 1] = sl[n];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int j = 0; j < kF32Chunk; ++j) {
+    const float vj = sv[j][dd];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = __builtin_fmaf(ss[n0 + 2 * u][j], vj, acc[u]);   // rows >= G unused
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int n = n0 + 2 * u;
+    if (n < p.G) {
+      const size_t part = part0 + (size_t)n * p.n_split_max;
+      p.ws_o[part * kD + dd] = acc[u];
+      if (dd == 0) {
+        p.ws_ml[2 * part] = sm[n];
+        p.ws_ml[2 * part + 1] = sl[n];
+      }
     }
   }
 }

@@ -83,8 +83,9 @@ int gqa_attn_version(void);
 /*
  * Number of keys each decode split (one workgroup's contiguous slice of one
  * sequence) covers for these arguments: `chunk_tokens` itself when it is
- * positive (it must then be a multiple of 128 for bf16, of 256 for f32), or
- * the library's automatic choice when it is 0.  Splits are contiguous
+ * positive (it must then be a multiple of 128 for bf16; the f32 path has a
+ * fixed split of 64 keys, so for f32 it must be 64), or the library's
+ * automatic choice when it is 0.  Splits are contiguous
  * position blocks, the placement the pages require for prefill/decode
  * sharing (§0 "CUBE Group", token-to-rank placement).  Returns a negative
  * gqa_status_t on invalid arguments.

@@ -50,7 +50,8 @@ def test_status_strings_and_version():
 
 def test_split_tokens_rules():
     L = binding.lib()
-    assert L.gqa_attn_decode_split_tokens(1, 1, 256, 0, F32) == 256
+    assert L.gqa_attn_decode_split_tokens(1, 1, 256, 0, F32) == 64
+    assert L.gqa_attn_decode_split_tokens(1, 1, 256, 64, F32) == 64
     assert L.gqa_attn_decode_split_tokens(1, 1, 256, 128, F32) == -INVALID
     assert L.gqa_attn_decode_split_tokens(1, 8, 32768, 384, BF16) == 384
     assert L.gqa_attn_decode_split_tokens(1, 8, 32768, 100, BF16) == -INVALID
