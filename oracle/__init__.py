@@ -21,6 +21,8 @@ invariants); none is "parity unpinned".
 from .attention import (  # noqa: F401
     attend_rows,
     decode,
+    decode_multi,
+    decode_multi_visible_len,
     prefill,
     prefill_visible_len,
     kv_head_of,

@@ -109,6 +109,52 @@ def decode(q, k_cache, v_cache, kv_lens, scale: float):
     return o, lse
 
 
+def decode_multi_visible_len(L: int, G: int, T_q: int):
+    """Visible key count of each M-folded row of a multi-token decode.
+
+    The ``T_q`` new tokens of a sequence of ``L`` valid positions are its last
+    ``T_q`` positions (their K/V rows are already in the cache, precondition
+    P4 of ADR-0060@5a76ed4 §0.5.1), so the query block starts at
+    ``q_start = L - T_q`` (``q_block_meta``, §0.5.3) and token ``t`` sees keys
+    ``j <= q_start + t``.  The G query heads are stacked head by head,
+    ``[G, T_q] -> [G*T_q]`` (§3 running state, §5.2): row ``r`` is token
+    ``r % T_q`` of head ``r // T_q``.
+    """
+    t = np.tile(np.arange(T_q, dtype=np.int64), G)
+    return (L - T_q) + t + 1
+
+
+def decode_multi(q, k_cache, v_cache, kv_lens, scale: float):
+    """Decode of ``T_q`` new tokens per sequence (multi-token / speculative
+    decode): the G heads x T_q tokens of one KV head are M-folded into
+    ``G*T_q`` rows that share every K/V tile (ADR-0060@5a76ed4 §3, §5.2),
+    with the causal tail of ``decode_multi_visible_len``.
+
+    q: ``[B, H_q, T_q, d]``; k_cache, v_cache: ``[B, H_kv, kv_cap, d]``;
+    kv_lens: ``[B]`` valid lengths, each ``>= T_q``.
+    Returns ``(o [B, H_q, T_q, d], lse [B, H_q, T_q])``.
+    """
+    q = np.asarray(q)
+    B, H_q, T_q, d = q.shape
+    H_kv = k_cache.shape[1]
+    G = H_q // H_kv
+    lens = np.asarray(kv_lens, dtype=np.int64).reshape(-1)
+    o = np.empty((B, H_q, T_q, d), dtype=np.float64)
+    lse = np.empty((B, H_q, T_q), dtype=np.float64)
+    for b in range(B):
+        L = int(lens[b])
+        if L < T_q:
+            raise ValueError("every sequence must hold its T_q new tokens")
+        vl = decode_multi_visible_len(L, G, T_q)
+        for kv in range(H_kv):
+            heads = [h for h in range(H_q) if kv_head_of(h, H_q, H_kv) == kv]
+            rows = q[b, heads].reshape(G * T_q, d)            # M-fold [G, T_q, d] -> [G*T_q, d]
+            ob, lb = attend_rows(rows, k_cache[b, kv, :L], v_cache[b, kv, :L], scale, vl)
+            o[b, heads] = ob.reshape(G, T_q, d)
+            lse[b, heads] = lb.reshape(G, T_q)
+    return o, lse
+
+
 def prefill_visible_len(rows, S_kv: int, causal: bool, causal_offset: int):
     """Visible key count per query row of a prefill chunk.
 

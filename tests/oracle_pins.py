@@ -17,7 +17,10 @@ package, or a mutant built by ``test_oracle_mutants.py``) and raises
   update equals one sweep for any tile size (§3 there); jointly permuting
   (key, value) pairs leaves decode unchanged; GQA equals multi-head attention
   with each KV head repeated G times; a causal prefill row equals a decode over
-  the keys it sees; huge logits do not overflow.
+  the keys it sees; huge logits do not overflow;
+* for the multi-token decode: brute force per new token, torch's SDPA with an
+  explicit mask, and its reductions to plain decode (T_q = 1, and each token
+  row over the keys it sees).
 
 Sizes keep the whole file to a few seconds of CPU.
 """
@@ -298,6 +301,73 @@ def pin_large_logits_and_nan_padding(O):
                atol=1e-9, what="large-logit lse")
 
 
+# ------------------------------------------------------ multi-token decode
+
+def pin_brute_force_decode_multi(O):
+    """Each new token, at position L - T_q + t, against high-precision brute
+    force over keys 0 .. L - T_q + t."""
+    rng = _rng(25)
+    for (B, H_q, H_kv, d, T_q, lens) in [(1, 2, 1, 4, 3, (5,)), (2, 4, 2, 4, 2, (2, 7)),
+                                         (2, 6, 2, 4, 4, (9, 4))]:
+        cap = max(lens) + 3
+        q = rng.standard_normal((B, H_q, T_q, d))
+        k = rng.standard_normal((B, H_kv, cap, d))
+        v = rng.standard_normal((B, H_kv, cap, d))
+        o, lse = O.decode_multi(q, k, v, np.array(lens), 0.6)
+        G = H_q // H_kv
+        for b in range(B):
+            for h in range(H_q):
+                for t in range(T_q):
+                    top = lens[b] - T_q + t + 1
+                    ro, rl = _mp_attention(q[b, h, t], k[b, h // G, :top],
+                                           v[b, h // G, :top], 0.6)
+                    _close(o[b, h, t], ro, what="brute decode_multi o")
+                    _close(lse[b, h, t], rl, what="brute decode_multi lse")
+
+
+def pin_decode_multi_sdpa(O):
+    """torch's float64 SDPA with GQA head sharing and an explicit boolean
+    mask (new token i of a sequence of length L sees keys j <= L - T_q + i)."""
+    rng = _rng(26)
+    B, H_q, H_kv, d, T_q = 3, 8, 2, 16, 5
+    lens = np.array([5, 12, 31])
+    q = rng.standard_normal((B, H_q, T_q, d))
+    k = rng.standard_normal((B, H_kv, 32, d))
+    v = rng.standard_normal((B, H_kv, 32, d))
+    o, _ = O.decode_multi(q, k, v, lens, 0.25)
+    for b in range(B):
+        L = int(lens[b])
+        mask = torch.arange(L)[None, :] <= (L - T_q) + torch.arange(T_q)[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[b:b + 1]), torch.from_numpy(k[b:b + 1, :, :L]),
+            torch.from_numpy(v[b:b + 1, :, :L]), attn_mask=mask, scale=0.25, enable_gqa=True)
+        _close(o[b:b + 1], ref.numpy(), what="decode_multi sdpa")
+
+
+def pin_decode_multi_special_cases(O):
+    """T_q = 1 is plain decode; every token row is a decode over the keys it
+    sees; with L = T_q the first token sees only key 0 (O = V[0], lse = s_0)."""
+    rng = _rng(27)
+    B, H_q, H_kv, d, T_q = 2, 4, 2, 8, 3
+    q = rng.standard_normal((B, H_q, T_q, d))
+    k = rng.standard_normal((B, H_kv, 10, d))
+    v = rng.standard_normal((B, H_kv, 10, d))
+    lens = np.array([10, 3])
+    o, lse = O.decode_multi(q, k, v, lens, 0.7)
+    for t in range(T_q):
+        od, ld = O.decode(q[:, :, t], k, v, lens - T_q + t + 1, 0.7)
+        _close(o[:, :, t], od, what="decode_multi row == decode")
+        _close(lse[:, :, t], ld, what="decode_multi lse == decode")
+    o1, l1 = O.decode_multi(q[:, :, :1], k, v, lens, 0.7)
+    od, ld = O.decode(q[:, :, 0], k, v, lens, 0.7)
+    _close(o1[:, :, 0], od, what="T_q=1 is decode")
+    _close(l1[:, :, 0], ld, what="T_q=1 lse")
+    for h in range(H_q):
+        _close(o[1, h, 0], v[1, h // 2, 0], what="L = T_q first token")
+        _close(lse[1, h, 0], 0.7 * float(np.dot(q[1, h, 0], k[1, h // 2, 0])),
+               what="L = T_q first token lse")
+
+
 PINS = [
     pin_brute_force_decode,
     pin_brute_force_prefill,
@@ -313,4 +383,7 @@ PINS = [
     pin_permutation_invariance,
     pin_gqa_is_repeated_mha,
     pin_large_logits_and_nan_padding,
+    pin_brute_force_decode_multi,
+    pin_decode_multi_sdpa,
+    pin_decode_multi_special_cases,
 ]

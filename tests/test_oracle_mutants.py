@@ -31,6 +31,11 @@ MUTANTS = {
     "partial_unshifted": ("p = np.exp(s - m[:, None])", "p = np.exp(s)"),
     "decode_drops_last_key": ("v_cache[b, kv, :L],\n", "v_cache[b, kv, 1:L + 1],\n"),
     "keys_reversed": ("s = float(scale) * (q @ k.T)", "s = float(scale) * (q @ k[::-1].T)"),
+    "multi_tail_short": ("return (L - T_q) + t + 1", "return (L - T_q) + t"),
+    "multi_fold_token_major": ("rows = q[b, heads].reshape(G * T_q, d)",
+                               "rows = q[b, heads].transpose(1, 0, 2).reshape(G * T_q, d)"),
+    "multi_tokens_repeated": ("t = np.tile(np.arange(T_q, dtype=np.int64), G)",
+                              "t = np.repeat(np.arange(T_q, dtype=np.int64), G)"),
     "visible_ignored": ("vis = np.arange(j0, j1)[None, :] < vl[:, None]",
                         "vis = np.arange(j0, j1)[None, :] < L + 0 * vl[:, None]"),
 }
