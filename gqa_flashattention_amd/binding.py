@@ -38,6 +38,14 @@ SIGNATURES = {
                                      _i, _i, _vp, _sz, _vp]),
     "gqa_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                               _f, _i, _vp]),
+    "gqa_attn_decode_multi_split_tokens": (_i, [_i, _i, _i, _i, _i, _i]),
+    "gqa_attn_decode_multi_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "gqa_attn_decode_multi": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
+                                   _i, _i, _vp, _sz, _vp]),
+    "gqa_attn_decode_multi_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                           _i, _f, _i, _i, _vp, _sz, _vp]),
+    "gqa_attn_decode_multi_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                           _i, _f, _i, _i, _vp, _sz, _vp]),
 }
 
 
@@ -141,6 +149,58 @@ def decode(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chunk_toke
           "combine": "gqa_attn_decode_combine"}[phase]
     st = getattr(lib(), fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens), _ptr(out),
                             _ptr(lse) if return_lse else None, B, H_q, H_kv, d, kv_cap,
+                            max_kv_len, scale, dt, chunk_tokens, _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, fn)
+    return (out, lse) if return_lse else out
+
+
+def decode_multi_split_tokens(B, H_kv, T_q, max_kv_len, chunk_tokens=0, dtype=DTYPE_BF16) -> int:
+    r = lib().gqa_attn_decode_multi_split_tokens(B, H_kv, T_q, max_kv_len, chunk_tokens, dtype)
+    if r < 0:
+        raise GQAError(-r, "gqa_attn_decode_multi_split_tokens")
+    return r
+
+
+def decode_multi_workspace_bytes(B, H_q, H_kv, d, T_q, max_kv_len, chunk_tokens=0,
+                                 dtype=DTYPE_BF16) -> int:
+    n = lib().gqa_attn_decode_multi_workspace_bytes(B, H_q, H_kv, d, T_q, max_kv_len,
+                                                    chunk_tokens, dtype)
+    if n == 0:
+        raise GQAError(1, "gqa_attn_decode_multi_workspace_bytes")
+    return n
+
+
+def decode_multi(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chunk_tokens=0,
+                 return_lse=False, out=None, lse=None, workspace=None, stream=None,
+                 phase="both"):
+    """``gqa_attn_decode_multi`` on torch tensors.
+
+    q ``[B,H_q,T_q,d]`` bf16 (token t of a sequence of length L sits at
+    position L - T_q + t), k_cache/v_cache ``[B,H_kv,kv_cap,d]`` bf16 holding
+    the new tokens' rows, kv_lens ``[B]`` int32 on the device.  ``phase`` as
+    for :func:`decode`.  Returns ``o`` (and ``lse`` ``[B,H_q,T_q]`` when
+    ``return_lse``).
+    """
+    _require_gpu(q, k_cache, v_cache, kv_lens)
+    B, H_q, T_q, d = q.shape
+    _, H_kv, kv_cap, _ = k_cache.shape
+    if kv_lens.dtype != torch.int32:
+        raise TypeError("kv_lens must be int32")
+    max_kv_len = kv_cap if max_kv_len is None else int(max_kv_len)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q, T_q), dtype=torch.float32, device=q.device)
+    need = decode_multi_workspace_bytes(B, H_q, H_kv, d, T_q, max_kv_len, chunk_tokens, dt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    fn = {"both": "gqa_attn_decode_multi", "partial": "gqa_attn_decode_multi_partial",
+          "combine": "gqa_attn_decode_multi_combine"}[phase]
+    st = getattr(lib(), fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens), _ptr(out),
+                            _ptr(lse) if return_lse else None, B, H_q, H_kv, d, T_q, kv_cap,
                             max_kv_len, scale, dt, chunk_tokens, _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, fn)

@@ -14,6 +14,7 @@ constexpr int kD = 128;
 constexpr int kMaxG = 16;          // query heads per KV head the decode MFMA tile holds
 constexpr int kF32Chunk = 64;      // keys per split of the fp32 decode path
 constexpr int kBf16ChunkQuantum = 128;  // 4 waves x 32-key blocks
+constexpr int kMultiMaxRows = 128;      // G * T_q rows of the multi-token decode tile
 constexpr size_t kWsAlign = 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -40,6 +41,30 @@ int split_tokens(int B, int H_kv, int max_kv_len, int chunk_tokens, int dtype) {
   c = (c + kBf16ChunkQuantum - 1) / kBf16ChunkQuantum * kBf16ChunkQuantum;
   if (c < 2 * kBf16ChunkQuantum) c = 2 * kBf16ChunkQuantum;
   if (c > 10 * kBf16ChunkQuantum) c = 10 * kBf16ChunkQuantum;
+  const long long cap = ((long long)max_kv_len + kBf16ChunkQuantum - 1) / kBf16ChunkQuantum * kBf16ChunkQuantum;
+  if (c > cap) c = cap;
+  return (int)c;
+}
+
+// Effective keys per multi-token decode split, or a negative status.
+int multi_split_tokens(int B, int H_kv, int T_q, int max_kv_len, int chunk_tokens, int dtype) {
+  if (B < 1 || H_kv < 1 || T_q < 1 || max_kv_len < 1 || chunk_tokens < 0)
+    return -GQA_ERR_INVALID_ARG;
+  if (T_q > max_kv_len) return -GQA_ERR_INVALID_ARG;
+  if (dtype == GQA_DTYPE_F32) return -GQA_ERR_UNSUPPORTED;
+  if (dtype != GQA_DTYPE_BF16) return -GQA_ERR_INVALID_ARG;
+  if (chunk_tokens > 0) {
+    if (chunk_tokens % kBf16ChunkQuantum != 0) return -GQA_ERR_INVALID_ARG;
+    return chunk_tokens;
+  }
+  // About 32 splits of the longest sequence, in multiples of 128 keys,
+  // between 256 and 2048 keys: one 32K-key sequence then fills the 256 CUs
+  // with one workgroup each, and a split's partial (G * T_q rows of d + 2
+  // floats) stays small against the K/V it covers.
+  long long c = ((long long)max_kv_len + 31) / 32;
+  c = (c + kBf16ChunkQuantum - 1) / kBf16ChunkQuantum * kBf16ChunkQuantum;
+  if (c < 2 * kBf16ChunkQuantum) c = 2 * kBf16ChunkQuantum;
+  if (c > 16 * kBf16ChunkQuantum) c = 16 * kBf16ChunkQuantum;
   const long long cap = ((long long)max_kv_len + kBf16ChunkQuantum - 1) / kBf16ChunkQuantum * kBf16ChunkQuantum;
   if (c > cap) c = cap;
   return (int)c;
@@ -72,7 +97,7 @@ const char* gqa_attn_status_string(int status) {
   }
 }
 
-int gqa_attn_version(void) { return 100; }
+int gqa_attn_version(void) { return 200; }
 
 int gqa_attn_decode_split_tokens(int B, int H_kv, int max_kv_len, int chunk_tokens, int dtype) {
   return split_tokens(B, H_kv, max_kv_len, chunk_tokens, dtype);
@@ -126,8 +151,11 @@ static int decode_phases(const void* q, const void* k_cache, const void* v_cache
   p.H_kv = H_kv;
   p.G = H_q / H_kv;
   p.kv_cap = kv_cap;
+  p.T_q = 1;
+  p.max_kv_len = max_kv_len;
   p.chunk = chunk;
   p.n_split_max = n_split;
+  p.q_negate = 0;
   p.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = gqa::launch_decode(p, dtype == GQA_DTYPE_BF16, static_cast<hipStream_t>(stream),
                                     phases);
@@ -162,6 +190,102 @@ int gqa_attn_decode_combine(const void* q, const void* k_cache, const void* v_ca
                        scale, dtype, chunk_tokens, workspace, workspace_bytes, stream,
                        gqa::kDecodeCombine);
 }
+
+int gqa_attn_decode_multi_split_tokens(int B, int H_kv, int T_q, int max_kv_len,
+                                       int chunk_tokens, int dtype) {
+  return multi_split_tokens(B, H_kv, T_q, max_kv_len, chunk_tokens, dtype);
+}
+
+size_t gqa_attn_decode_multi_workspace_bytes(int B, int H_q, int H_kv, int d, int T_q,
+                                             int max_kv_len, int chunk_tokens, int dtype) {
+  if (H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || d != kD) return 0;
+  if ((long long)(H_q / H_kv) * T_q > kMultiMaxRows) return 0;
+  const int chunk = multi_split_tokens(B, H_kv, T_q, max_kv_len, chunk_tokens, dtype);
+  if (chunk <= 0) return 0;
+  const int n_split = (max_kv_len + chunk - 1) / chunk;
+  return ws_layout(B, H_q * T_q, n_split).total;
+}
+
+static int decode_multi_phases(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* kv_lens, void* o, float* lse, int B, int H_q,
+                               int H_kv, int d, int T_q, int kv_cap, int max_kv_len, float scale,
+                               int dtype, int chunk_tokens, void* workspace,
+                               size_t workspace_bytes, void* stream, int phases) {
+  if (!q || !k_cache || !v_cache || !kv_lens || !o) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return GQA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(kv_lens) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return GQA_ERR_INVALID_ARG;
+  if (B < 1 || H_q < 1 || H_kv < 1 || d < 1 || T_q < 1 || kv_cap < 1 || max_kv_len < 1)
+    return GQA_ERR_INVALID_ARG;
+  if (H_q % H_kv != 0 || max_kv_len > kv_cap || T_q > max_kv_len) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16) return GQA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (chunk_tokens < 0) return GQA_ERR_INVALID_ARG;
+  if (B > 65535 || H_kv > 65535) return GQA_ERR_INVALID_ARG;
+  if ((long long)B * H_q * T_q > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
+  if (d != kD || dtype != GQA_DTYPE_BF16 || (long long)(H_q / H_kv) * T_q > kMultiMaxRows)
+    return GQA_ERR_UNSUPPORTED;
+  const int chunk = multi_split_tokens(B, H_kv, T_q, max_kv_len, chunk_tokens, dtype);
+  if (chunk <= 0) return GQA_ERR_INVALID_ARG;
+  const int n_split = (max_kv_len + chunk - 1) / chunk;
+  const WsLayout wl = ws_layout(B, H_q * T_q, n_split);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u)) return GQA_ERR_WORKSPACE;
+  if (workspace_bytes < wl.total) return GQA_ERR_WORKSPACE;
+
+  gqa::DecodeParams p;
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.kv_lens = kv_lens;
+  p.o = o;
+  p.lse = lse;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+  p.B = B;
+  p.H_q = H_q;
+  p.H_kv = H_kv;
+  p.G = H_q / H_kv;
+  p.kv_cap = kv_cap;
+  p.T_q = T_q;
+  p.max_kv_len = max_kv_len;
+  p.chunk = chunk;
+  p.n_split_max = n_split;
+  p.q_negate = scale < 0.f;
+  p.scale_log2 = fabsf(scale) * 1.4426950408889634f;
+  hipError_t e = gqa::launch_decode_multi(p, static_cast<hipStream_t>(stream), phases);
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+#define GQA_MULTI_ARGS                                                                        \
+  q, k_cache, v_cache, kv_lens, o, lse, B, H_q, H_kv, d, T_q, kv_cap, max_kv_len, scale, dtype, \
+      chunk_tokens, workspace, workspace_bytes, stream
+
+int gqa_attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
+                          int d, int T_q, int kv_cap, int max_kv_len, float scale, int dtype,
+                          int chunk_tokens, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return decode_multi_phases(GQA_MULTI_ARGS, gqa::kDecodePartial | gqa::kDecodeCombine);
+}
+
+int gqa_attn_decode_multi_partial(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* kv_lens, void* o, float* lse, int B, int H_q,
+                                  int H_kv, int d, int T_q, int kv_cap, int max_kv_len,
+                                  float scale, int dtype, int chunk_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return decode_multi_phases(GQA_MULTI_ARGS, gqa::kDecodePartial);
+}
+
+int gqa_attn_decode_multi_combine(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* kv_lens, void* o, float* lse, int B, int H_q,
+                                  int H_kv, int d, int T_q, int kv_cap, int max_kv_len,
+                                  float scale, int dtype, int chunk_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return decode_multi_phases(GQA_MULTI_ARGS, gqa::kDecodeCombine);
+}
+
+#undef GQA_MULTI_ARGS
 
 int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int H_q, int H_kv, int d, int S_q, int S_kv, int kv_cap, int causal,

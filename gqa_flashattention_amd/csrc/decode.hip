@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const int L = p.kv_lens[b];
+  const int L = min(p.kv_lens[b], p.max_kv_len);
   const int start = split * p.chunk;
   if (start >= L) return;
   const int end = min(start + p.chunk, L);
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p)
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const int L = p.kv_lens[b];
+  const int L = min(p.kv_lens[b], p.max_kv_len);
   const int start = split * kF32Chunk;
   if (start >= L) return;
   const int cnt = min(kF32Chunk, L - start);
@@ -413,18 +413,18 @@ __device__ __forceinline__ void merge_group(MergeAcc& st, const float* ml, const
   st.M = gm;
 }
 
-// Combine: one workgroup of 128 threads per (sequence, query head); 4 groups
+// Combine: one workgroup of 128 threads per (sequence, query head, token); 4 groups
 // of 32 threads take every 4th split, thread t covers output columns
 // 4*(t%32) .. +4, and the groups merge through LDS.  Normalises once and
 // rounds to the output dtype (the final O / l of §4).
 template <typename OutT>
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
-  const int bh = blockIdx.x;
-  const int b = bh / p.H_q;
+  const int bh = blockIdx.x;                 // folded row (sequence, head, token)
+  const int b = bh / (p.H_q * p.T_q);
   const int t = threadIdx.x;
   const int grp = t >> 5;
   const int d0 = (t & 31) * 4;
-  const int L = p.kv_lens[b];
+  const int L = min(p.kv_lens[b], p.max_kv_len);
   const int ns = (L + p.chunk - 1) / p.chunk;
   const size_t part0 = (size_t)bh * p.n_split_max;
   MergeAcc st{kNegInf, {0.f, 0.f, 0.f, 0.f}, 0.f};
@@ -463,9 +463,9 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, i
   }
   if (phases & kDecodeCombine) {
     if (bf16) {
-      hipLaunchKernelGGL(decode_combine_kernel<__bf16>, dim3(p.B * p.H_q), dim3(128), 0, stream, p);
+      hipLaunchKernelGGL(decode_combine_kernel<__bf16>, dim3(p.B * p.H_q * p.T_q), dim3(128), 0, stream, p);
     } else {
-      hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(p.B * p.H_q), dim3(128), 0, stream, p);
+      hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(p.B * p.H_q * p.T_q), dim3(128), 0, stream, p);
     }
   }
   return hipGetLastError();

@@ -1,0 +1,386 @@
+// Multi-token decode for gfx950: T_q new tokens per sequence (speculative or
+// short-chunk decode), each attending causally to the cache that already
+// holds all T_q of them.  Split-KV partial kernel; the partials are merged
+// by the decode combine kernel.
+//
+// Method: ADR-0060 "AHBM GQA Fused Attention Kernel (Llama3-70B)", revision
+// 5a76ed4 -- §3 (running state m, l of shape [G, T_q] and O of [G, T_q, d]:
+// the G heads x T_q tokens of one KV head are stacked into the M rows of one
+// GEMM, so every K/V tile is streamed once for all of them; additive causal
+// mask on boundary tiles only), §5.2 (the same M-fold for decode),
+// §0.5.3 (q_block_meta: the block of T_q queries starts at q_start =
+// L - T_q, so token t sees keys j <= L - T_q + t) and §4 (unnormalised
+// (m, l, O) partials merged by log-sum-exp).
+//
+// GPU mapping.  One workgroup = 4 waves = one contiguous split of one
+// (sequence, KV head).  The M = G*T_q folded rows (row r = token r % T_q of
+// head r / T_q, the memory order of q) form R = 1, 2 or 4 groups of 32;
+// wave w takes row group w % R and key slot w / R, so the 4 waves cover
+// R row groups x 4/R key slots.  A step stages 32 keys per key slot of K and
+// V in LDS (direct global -> LDS loads into a ring of steps, shared by the
+// waves of different row groups) and each wave folds its 32 keys into its
+// 32 rows:
+//   S^T = K . Q^T on the 32x32x16 bf16 MFMA (keys in M, rows in N), so a
+//   lane holds 16 scores of one row (the other 16 sit in lane ^ 32);
+//   P = exp2(S*scale - ref) rounded to bf16 is directly the B operand of
+//   O^T = V^T . P^T, whose V^T operand comes from the row-major V tile
+//   through the transposing LDS read.
+// Softmax statistics use the lazy reference of the prefill kernel: weights
+// are taken relative to a per-row reference that moves only when a score
+// exceeds it by more than 64 (log2 units), detected by the lane sum of the
+// weights; O and l share the reference, so the partial (ref, l, O) is an
+// exact (m, l, O) triple for the log-sum-exp merge.  At the end the key
+// slots of a row group merge through LDS and one partial per (row, split) is
+// written.
+//
+// Only the last steps of a sequence need the causal tail mask (the T_q - 1
+// last keys are not visible to every token); earlier steps run unmasked.
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "lds_tile.hpp"
+
+namespace gqa {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSub = 32;               // keys per wave per step
+constexpr int kRowBytes = kD * 2;      // one bf16 K or V row
+
+constexpr float kResetGap = 64.f;                       // log2 units
+constexpr float kPsumLimit = 18446744073709551616.f;    // 2^64 = exp2(kResetGap)
+constexpr float kRefBelow = 32.f;
+
+template <int N>
+using Int = std::integral_constant<int, N>;
+
+// Geometry for R row groups of 32.
+template <int R>
+struct MqShape {
+  static constexpr int kSlots = kWaves / R;               // key slots
+  static constexpr int kStep = kSub * kSlots;             // keys per step (128, 64, 32)
+  static constexpr int kStepBytes = kStep * kRowBytes;    // K (or V) bytes of one step
+  static constexpr int kRing = R == 4 ? 3 : 2;            // steps resident in LDS
+  static constexpr int kInsts = kStep / 4 / kWaves;       // 1 KiB loads per wave per step, K or V
+  static constexpr int kOcc = R == 1 ? 1 : 2;             // workgroups per CU (LDS bound for R = 1)
+};
+
+// LDS block of one wave's row-group state for the merge of key slots:
+// 32 rows x (128 O + m + l + 2 pad) floats.
+constexpr int kRedStride = kD + 4;
+constexpr int kRedFloats = 32 * kRedStride;
+
+}  // namespace
+
+// Grid: (n_split_max, H_kv, B); block: 256 threads.
+template <int R>
+__global__ __launch_bounds__(kThreads, MqShape<R>::kOcc) void decode_multi_partial_kernel(
+    DecodeParams p) {
+  using S = MqShape<R>;
+  // K ring then V ring, contiguous so that the merge can reuse both.
+  __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][S::kRing][S::kStep * kD];
+
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int L = min(p.kv_lens[b], p.max_kv_len);
+  const int start = split * p.chunk;
+  if (start >= L) return;
+  const int end = min(start + p.chunk, L);
+  const int nsteps = (end - start + S::kStep - 1) / S::kStep;
+  // Steps [0, n_full) hold only keys every row sees (keys below L - T_q + 1).
+  const int n_full = max(0, min(L - p.T_q + 1, end) - start) / S::kStep;
+
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  const int rg = wave % R;      // row group
+  const int kq = wave / R;      // key slot
+  const int c = lane & 31;      // row of this lane within the row group
+  const int h2 = lane >> 5;
+  const int t16 = lane & 15;
+  const int gamma = lane >> 4;
+
+  const int M = p.G * p.T_q;
+  const int row = 32 * rg + c;
+  const bool row_ok = row < M;
+  // Last key this lane's row may see within the split (padding rows see all).
+  const int vis_last = row_ok ? min(L - p.T_q + row % p.T_q, end - 1) : end - 1;
+
+  const size_t row0 = ((size_t)b * p.H_q + (size_t)kvh * p.G) * p.T_q;   // first folded row
+  const __bf16* Kg = static_cast<const __bf16*>(p.k) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
+  const __bf16* Vg = static_cast<const __bf16*>(p.v) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
+
+  // Q^T operand (B of S^T): row `row`, d = 16*kk + 8*h2 .. +8.  A negative
+  // scale is applied exactly by flipping Q's sign bits.
+  bf16x8 qb[8];
+  {
+    const __bf16* qr = static_cast<const __bf16*>(p.q) + (row0 + (row_ok ? row : 0)) * kD + 8 * h2;
+    const unsigned flip = p.q_negate ? 0x80008000u : 0u;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      u32x4 v = row_ok ? ld16(qr + 16 * kk) : u32x4{0, 0, 0, 0};
+      v ^= u32x4{flip, flip, flip, flip};
+      qb[kk] = as_bf16x8(v);
+    }
+  }
+
+  // Per-lane LDS addresses of the MFMA operands in ring slot 0 (other slots
+  // are immediate offsets), hidden from the compiler so that it keeps the
+  // offsets in the instructions.
+  //  K (A of S^T), k-step kk: row 32*kq + c, logical piece 2*kk + h2.
+  //  V (A of O^T, transposing read), key step st, d-tile dt: rows
+  //    32*kq + 16*st + 4*h2 + t16/4 and 8 rows further, d = 32*dt +
+  //    16*(gamma&1) + 4*(t16&3) .. +4; the lane receives V^T column
+  //    d = 32*dt + 16*(gamma&1) + t16.
+  const unsigned lds_k0 = lds_addr(&sKV[0][0][0]);
+  const unsigned lds_v0 = lds_addr(&sKV[1][0][0]);
+  unsigned kaddr[8], vaddr[4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    kaddr[kk] = lds_k0 + (32 * kq + c) * kRowBytes + 16 * k_swz(c, 2 * kk + h2);
+    asm volatile("" : "+v"(kaddr[kk]));
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int r0 = 32 * kq + 4 * h2 + (t16 >> 2);
+    const int e = 32 * dt + 16 * (gamma & 1) + 4 * (t16 & 3);
+    vaddr[dt] = lds_v0 + r0 * kRowBytes + 16 * v_swz(r0, e >> 3) + 2 * (e & 7);
+    asm volatile("" : "+v"(vaddr[dt]));
+  }
+
+  // Direct global -> LDS loads of one step: the waves split the step's row
+  // groups of 4; lane l lands at physical piece l%16 of row 4*group + l/16
+  // and fetches the logical piece that belongs there.  The buffer resource
+  // ends at the split's last key, so rows past it read as zeros (masked,
+  // with zero V rows) and nothing outside the split is read.
+  int ld_off[2][S::kInsts];
+#pragma unroll
+  for (int i = 0; i < S::kInsts; ++i) {
+    const int r = 4 * (S::kInsts * wave + i) + (lane >> 4);
+    ld_off[0][i] = r * kRowBytes + 16 * k_swz(r, lane & 15);   // XOR is an involution
+    ld_off[1][i] = r * kRowBytes + 16 * v_swz(r, lane & 15);
+  }
+  auto load_step = [&](auto slot_c, int s) {
+    constexpr int slot = decltype(slot_c)::value;
+    const int key0 = start + s * S::kStep;
+    const unsigned bytes = (unsigned)(end - key0) * kRowBytes;
+    const u32x4 rk = buffer_rsrc(Kg + (size_t)key0 * kD, bytes);
+    const u32x4 rv = buffer_rsrc(Vg + (size_t)key0 * kD, bytes);
+#pragma unroll
+    for (int i = 0; i < S::kInsts; ++i)
+      dma_load_x4(ld_off[0][i], rk, lds_k0 + slot * S::kStepBytes + 4 * (S::kInsts * wave + i) * kRowBytes);
+#pragma unroll
+    for (int i = 0; i < S::kInsts; ++i)
+      dma_load_x4(ld_off[1][i], rv, lds_v0 + slot * S::kStepBytes + 4 * (S::kInsts * wave + i) * kRowBytes);
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float m_ref = kNegInf;   // reference (log2 units) of this lane's row, same on both halves
+  float lpart = 0.f;       // this lane's half of the running sum, relative to m_ref
+  // |scale| * log2(e), kept away from zero so that masked (-inf) scores
+  // stay -inf.
+  const float sl2 = fmaxf(p.scale_log2, 1e-30f);
+
+  // P = exp2(S*scale - ref) of the lane's 16 scores, rounded to bf16 in the
+  // P^T operand layout (key step st: keys 16*st + {0..3, 8..11} + 4*h2);
+  // returns their fp32 sum.
+  auto exps = [&](const f32x16& sacc, float negr, u32x4 (&pw)[2]) -> float {
+    float psum = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float e0 = fast_exp2(__builtin_fmaf(sacc[8 * st + 2 * jj], sl2, negr));
+        const float e1 = fast_exp2(__builtin_fmaf(sacc[8 * st + 2 * jj + 1], sl2, negr));
+        psum += e0 + e1;
+        pw[st][jj] = pack_bf16x2(e0, e1);
+      }
+    return psum;
+  };
+
+  // Step s: scores of this wave's 32 keys against its 32 rows, the tail
+  // mask (last steps only), the softmax against the reference, and P.V.
+  auto compute = [&](auto slot_c, int s) {
+    constexpr int slot = decltype(slot_c)::value;
+    f32x16 sacc;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 a = *lds_ptr<bf16x8>(kaddr[kk] + slot * S::kStepBytes);
+      const f32x16 zero = {};
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kk], kk ? sacc : zero, 0, 0, 0);
+    }
+    if (s >= n_full) {
+      const int key0 = start + s * S::kStep + 32 * kq;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + 8 * (i >> 2) + 4 * h2 + (i & 3);
+        if (key > vis_last) sacc[i] = kNegInf;
+      }
+    }
+    u32x4 pw[2];
+    float psum = exps(sacc, -m_ref, pw);
+    if (__any(!(psum <= kPsumLimit))) {
+      // Some weight exceeds 2^64 (a score more than 64 above the reference,
+      // always so on a row's first visible keys): move the reference of
+      // such rows to 32 below their max, rescale O and l, redo P.  A row
+      // with no visible key yet keeps the reference -inf and gets P = 0.
+      float hmax = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) hmax = fmaxf(hmax, sacc[i]);
+      const float rmax = wave_max_xor(hmax, 32) * sl2;
+      const float m_new = rmax > m_ref + kResetGap ? rmax - kRefBelow : m_ref;
+      const float corr = m_new == m_ref ? 1.f : fast_exp2(m_ref - m_new);
+      lpart *= corr;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= corr;
+      m_ref = m_new;
+      psum = exps(sacc, m_ref == kNegInf ? 0.f : -m_ref, pw);
+    }
+    lpart += psum;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8 pb = as_bf16x8(pw[st]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const unsigned a = vaddr[dt] + slot * S::kStepBytes + 4096 * st;
+        const u32x2 w0 = __builtin_bit_cast(u32x2, lds_read_tr16(a));
+        const u32x2 w1 = __builtin_bit_cast(u32x2, lds_read_tr16(a + 8 * kRowBytes));
+        const u32x4 av = {w0[0], w0[1], w1[0], w1[1]};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), pb, o[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  // Ring schedule: steps 0 .. kRing-2 are loaded up front; step s waits for
+  // its own loads (leaving later steps' loads in flight), meets the other
+  // waves at a barrier (their loads of step s have landed, and all are done
+  // with step s-1, whose slot is refilled next), issues the load of step
+  // s + kRing - 1 and computes.
+  auto step = [&](auto slot_c, int s) {
+    constexpr int slot = decltype(slot_c)::value;
+    if (S::kRing == 3 && s + 1 < nsteps) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::kInsts));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __syncthreads();
+    if (s + S::kRing - 1 < nsteps) load_step(Int<(slot + S::kRing - 1) % S::kRing>(), s + S::kRing - 1);
+    compute(slot_c, s);
+  };
+
+  load_step(Int<0>(), 0);
+  if (S::kRing == 3 && nsteps > 1) load_step(Int<1 % S::kRing>(), 1);
+  int s = 0;
+  for (; s + S::kRing <= nsteps; s += S::kRing) {
+    step(Int<0>(), s);
+    step(Int<1>(), s + 1);
+    if constexpr (S::kRing == 3) step(Int<2 % S::kRing>(), s + 2);
+  }
+  if (s < nsteps) step(Int<0>(), s);
+  if (S::kRing == 3 && s + 1 < nsteps) step(Int<1>(), s + 1);
+
+  // Row sums over both halves; merge the key slots of each row group.
+  const float lrow = lpart + __shfl_xor(lpart, 32, 64);
+  float m_out = m_ref, l_out = lrow;
+  if constexpr (S::kSlots > 1) {
+    float* red = reinterpret_cast<float*>(&sKV[0][0][0]);
+    static_assert((S::kSlots - 1) * R * kRedFloats * 4 <= (int)sizeof(sKV), "merge buffer");
+    __syncthreads();   // all waves are done with the ring (every load was waited for)
+    if (kq > 0) {
+      float* mine = red + ((kq - 1) * R + rg) * kRedFloats + c * kRedStride;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 v = {o[dt][4 * i4], o[dt][4 * i4 + 1], o[dt][4 * i4 + 2], o[dt][4 * i4 + 3]};
+          *reinterpret_cast<f32x4*>(mine + 32 * dt + 8 * i4 + 4 * h2) = v;
+        }
+      if (h2 == 0) {
+        mine[kD] = m_ref;
+        mine[kD + 1] = lrow;
+      }
+    }
+    __syncthreads();
+    if (kq > 0) return;
+    float mk[S::kSlots];
+    mk[0] = m_ref;
+    float mmax = m_ref;
+#pragma unroll
+    for (int k = 1; k < S::kSlots; ++k) {
+      mk[k] = red[((k - 1) * R + rg) * kRedFloats + c * kRedStride + kD];
+      mmax = fmaxf(mmax, mk[k]);
+    }
+    const float w0 = mk[0] == kNegInf ? 0.f : fast_exp2(mk[0] - mmax);
+    l_out = lrow * w0;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] *= w0;
+#pragma unroll
+    for (int k = 1; k < S::kSlots; ++k) {
+      const float* other = red + ((k - 1) * R + rg) * kRedFloats + c * kRedStride;
+      const float wk = mk[k] == kNegInf ? 0.f : fast_exp2(mk[k] - mmax);
+      l_out += wk * other[kD + 1];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(other + 32 * dt + 8 * i4 + 4 * h2);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[dt][4 * i4 + u] += wk * v[u];
+        }
+    }
+    m_out = mmax;
+  }
+
+  // The partial of (row, split): O in the lane's d = 32*dt + 8*i4 + 4*h2
+  // .. +4, and (m, l) from the first half.
+  if (row_ok) {
+    const size_t part = (row0 + row) * p.n_split_max + split;
+    float* wo = p.ws_o + part * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 v = {o[dt][4 * i4], o[dt][4 * i4 + 1], o[dt][4 * i4 + 2], o[dt][4 * i4 + 3]};
+        *reinterpret_cast<f32x4*>(wo + 32 * dt + 8 * i4 + 4 * h2) = v;
+      }
+    if (h2 == 0) {
+      p.ws_ml[2 * part] = m_out;
+      p.ws_ml[2 * part + 1] = l_out;
+    }
+  }
+}
+
+int decode_multi_row_groups(int M) { return M <= 32 ? 1 : (M <= 64 ? 2 : 4); }
+
+hipError_t launch_decode_multi(const DecodeParams& p, hipStream_t stream, int phases) {
+  if (phases & kDecodePartial) {
+    const dim3 grid(p.n_split_max, p.H_kv, p.B);
+    switch (decode_multi_row_groups(p.G * p.T_q)) {
+      case 1:
+        hipLaunchKernelGGL(decode_multi_partial_kernel<1>, grid, dim3(kThreads), 0, stream, p);
+        break;
+      case 2:
+        hipLaunchKernelGGL(decode_multi_partial_kernel<2>, grid, dim3(kThreads), 0, stream, p);
+        break;
+      default:
+        hipLaunchKernelGGL(decode_multi_partial_kernel<4>, grid, dim3(kThreads), 0, stream, p);
+        break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & kDecodeCombine) return launch_decode(p, true, stream, kDecodeCombine);
+  return hipSuccess;
+}
+
+}  // namespace gqa

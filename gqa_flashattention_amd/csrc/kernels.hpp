@@ -8,18 +8,21 @@
 namespace gqa {
 
 struct DecodeParams {
-  const void* q;        // [B, H_q, d]
+  const void* q;        // [B, H_q, T_q, d]
   const void* k;        // [B, H_kv, kv_cap, d]
   const void* v;        // [B, H_kv, kv_cap, d]
-  const int32_t* kv_lens;  // [B] device
-  void* o;              // [B, H_q, d]
-  float* lse;           // [B, H_q] or null
-  float* ws_o;          // [B, H_q, n_split_max, d] unnormalised partial O
-  float* ws_ml;         // [B, H_q, n_split_max, 2] partial (m in log2 units, l)
+  const int32_t* kv_lens;  // [B] device (used as min(kv_lens[b], max_kv_len))
+  void* o;              // [B, H_q, T_q, d]
+  float* lse;           // [B, H_q, T_q] or null
+  float* ws_o;          // [B, H_q, T_q, n_split_max, d] unnormalised partial O
+  float* ws_ml;         // [B, H_q, T_q, n_split_max, 2] partial (m in log2 units, l)
   int B, H_q, H_kv, G, kv_cap;
+  int T_q;              // new tokens per sequence (1 for gqa_attn_decode)
+  int max_kv_len;
   int chunk;            // keys per split
   int n_split_max;      // ceil(max_kv_len / chunk)
-  float scale_log2;     // scale * log2(e)
+  int q_negate;         // multi-token path: 1 when the scale is negative (Q's sign is flipped)
+  float scale_log2;     // scale * log2(e); |scale| * log2(e) on the multi-token path
 };
 
 struct PrefillParams {
@@ -41,6 +44,11 @@ constexpr int kDecodePartial = 1;
 constexpr int kDecodeCombine = 2;
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, int phases);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+// Multi-token decode: its partial kernel (chosen by G * T_q) and/or the
+// decode combine over the B * H_q * T_q rows.
+hipError_t launch_decode_multi(const DecodeParams& p, hipStream_t stream, int phases);
+// Row groups of 32 the multi-token partial kernel uses for M = G * T_q rows.
+int decode_multi_row_groups(int M);
 
 // Query heads of one KV group a prefill workgroup covers, and the query rows
 // (heads x positions) of one workgroup.

@@ -48,6 +48,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tile.hpp"
 
 namespace gqa {
 
@@ -64,27 +65,7 @@ constexpr float kResetGap = 64.f;    // log2 units
 constexpr float kPsumLimit = 18446744073709551616.f;   // 2^64 = exp2(kResetGap)
 constexpr float kRefBelow = 32.f;
 
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
 constexpr int kTileBytes = kTileElems * 2;
-
-// 32-bit LDS address of a shared-memory object, and back.
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-template <typename T>
-__device__ __forceinline__ const __attribute__((address_space(3))) T* lds_ptr(unsigned a) {
-  return (const __attribute__((address_space(3))) T*)(uintptr_t)a;
-}
-
-__device__ __forceinline__ s16x4 lds_read_tr16(unsigned a) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a);
-}
-
-// Physical 16-byte piece of logical piece `pc` (0..15) in tile row `row`.
-__device__ __forceinline__ int k_swz(int row, int pc) { return pc ^ (row & 15); }
-__device__ __forceinline__ int v_swz(int row, int pc) { return pc ^ ((row & 3) << 2); }
 
 struct Tile16 {
   f32x16 s[2];   // S^T of keys kbase + 32*mt + 8*(i/4) + 4*h2 + (i%4), query c
@@ -219,22 +200,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // addresses apart).  All loads are waited for before each barrier.
   auto tile_load_part = [&](int kv, int buf, int tile, int i) {
     tile = min(tile, ntiles - 1);
-    const uintptr_t a = reinterpret_cast<uintptr_t>(kv ? Vg : Kg) + (size_t)tile * (kBN * kD * 2);
-    u32x4 rsrc;
-    rsrc[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
-    rsrc[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu);   // stride 0
-    rsrc[2] = __builtin_amdgcn_readfirstlane((unsigned)(p.S_kv - tile * kBN) * (kD * 2));
-    rsrc[3] = 0x00020000u;                     // raw buffer, 32-bit data format
-    const unsigned dst = __builtin_amdgcn_readfirstlane(
-        (kv ? lds_v0 : lds_k0) + buf * kTileBytes + 4 * (kInsts * wave + i) * kD * 2);
-    // Wait states inside the statement (the compiler's hazard checks do not
-    // look into inline assembly): the descriptor and M0 value were just
-    // written by VALU (v_readfirstlane), and an LDS DMA may not follow an
-    // M0 write directly.
-    asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(ld_off[kv][i]), "s"(rsrc), "s"(dst)
-                 : "memory");
+    const u32x4 rsrc = buffer_rsrc((kv ? Vg : Kg) + (size_t)tile * (kBN * kD),
+                                   (unsigned)(p.S_kv - tile * kBN) * (kD * 2));
+    dma_load_x4(ld_off[kv][i], rsrc,
+                (kv ? lds_v0 : lds_k0) + buf * kTileBytes + 4 * (kInsts * wave + i) * kD * 2);
   };
   auto tile_load = [&](int kv, int buf, int tile) {
 #pragma unroll
@@ -416,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     u32x4* z = reinterpret_cast<u32x4*>(sV[3]);
     for (int i = t; i < kTileElems / 8; i += kThreads) z[i] = u32x4{0, 0, 0, 0};
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile loads landed
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's tile loads landed
   __syncthreads();
   Tile16 T;
   PTile PA, PB;
@@ -462,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       tile_load(0, (2 * G + 3) % 4, j + 3);
       tile_load(0, (2 * G + 4) % 4, j + 4);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
   };
   for (int j = 0; j < ntiles; j += 4) {

@@ -28,7 +28,7 @@ import torch
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "decode" or "prefill"
+    kind: str            # "decode", "decode_multi" or "prefill"
     B: int
     H_q: int
     H_kv: int
@@ -40,6 +40,7 @@ class Workload:
     S_kv: int = 0        # prefill: keys in the cache
     causal: bool = True
     offset: int = 0      # prefill: cached tokens before the chunk
+    T_q: int = 1         # decode_multi: new tokens per sequence (the last T_q positions)
 
     @property
     def G(self) -> int:
@@ -59,16 +60,24 @@ class Workload:
 
     @property
     def max_kv_len(self) -> int:
-        return max(self.lens) if self.kind == "decode" else self.S_kv
+        return max(self.lens) if self.kind.startswith("decode") else self.S_kv
 
     def kv_bytes(self) -> int:
         """K+V bytes a decode step must read: valid keys only, padding excluded."""
         return 2 * sum(self.lens) * self.H_kv * self.d * self.elem_bytes
 
     def decode_bytes(self) -> int:
-        """Algorithmic bytes of one decode call: K+V of the valid keys, Q and O."""
-        qo = 2 * self.B * self.H_q * self.d * self.elem_bytes
+        """Algorithmic bytes of one decode call: K+V of the valid keys, Q and O
+        (T_q rows per head for the multi-token decode)."""
+        qo = 2 * self.B * self.H_q * self.T_q * self.d * self.elem_bytes
         return self.kv_bytes() + qo
+
+    def decode_multi_flops(self) -> int:
+        """Algorithmic FLOPs of a multi-token decode: 4*d per visible
+        (token, key) pair and query head; token t of a sequence of length L
+        sees L - T_q + t + 1 keys."""
+        pairs = sum(self.T_q * (L - self.T_q) + self.T_q * (self.T_q + 1) // 2 for L in self.lens)
+        return 4 * self.d * self.H_q * pairs
 
     def visible_pairs_per_head(self) -> int:
         """(query, key) pairs a causal prefill chunk must score, per head."""
@@ -96,6 +105,14 @@ WORKLOADS = {
     "prefill_chunk_64k": Workload("prefill_chunk_64k", "prefill", B=1, H_q=64,
                                   H_kv=8, d=128, dtype="bf16", S_q=8192,
                                   S_kv=65536, causal=True, offset=57344),
+    # Multi-token (speculative) decode on the 32K-key cache: 4 and 16 new
+    # tokens per sequence, G*T_q = 32 and 128 folded rows.
+    "decode_multi_llama70b_32k_t4": Workload("decode_multi_llama70b_32k_t4", "decode_multi",
+                                             B=1, H_q=64, H_kv=8, d=128, dtype="bf16",
+                                             lens=(32768,), kv_cap=32768, T_q=4),
+    "decode_multi_llama70b_32k_t16": Workload("decode_multi_llama70b_32k_t16", "decode_multi",
+                                              B=1, H_q=64, H_kv=8, d=128, dtype="bf16",
+                                              lens=(32768,), kv_cap=32768, T_q=16),
 }
 
 # Seed per workload: 20260000 + its position in the list above (1-based).
@@ -130,6 +147,15 @@ def make_decode(w: Workload, device="cpu", seed=None, nan_pad=True, lens=None):
                 v[b, :, L:].fill_(float("nan"))
     kv_lens = torch.tensor(lens, dtype=torch.int32, device=device)
     return {"q": q, "k": k, "v": v, "kv_lens": kv_lens}
+
+
+def make_decode_multi(w: Workload, device="cpu", seed=None, nan_pad=True, lens=None):
+    """Multi-token decode inputs: q ``[B,H_q,T_q,d]``, k/v ``[B,H_kv,kv_cap,d]``
+    (the new tokens' rows included), kv_lens int32."""
+    x = make_decode(w, device=device, seed=seed, nan_pad=nan_pad, lens=lens)
+    seed = SEEDS.get(w.name, 1) if seed is None else seed
+    x["q"] = randn((w.B, w.H_q, w.T_q, w.d), w.torch_dtype, device, seed, 3)
+    return x
 
 
 def make_prefill(w: Workload, device="cpu", seed=None, nan_pad=True, kv_cap=None):

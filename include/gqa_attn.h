@@ -10,6 +10,11 @@
  *                     merged by a log-sum-exp combine.
  *   gqa_attn_prefill  a chunk of S_q query tokens, optionally causal with an
  *                     offset (the chunk follows causal_offset cached tokens).
+ *   gqa_attn_decode_multi
+ *                     T_q >= 1 new tokens per sequence (speculative or
+ *                     short-chunk decode) against the cache that holds them:
+ *                     the G heads x T_q tokens of a KV head are M-folded
+ *                     into one tile; split-KV partials merged as for decode.
  *
  * Source of the operation: ADR-0060 "AHBM GQA Fused Attention Kernel
  * (Llama3-70B)", kernbench2 revision 5a76ed4: "Algorithm lineage" (exact
@@ -23,9 +28,11 @@
  *    must be 16-byte aligned.  Tensors are dense, row-major, head-major, with
  *    the head dimension d innermost:
  *        q (decode)   [B, H_q, d]          q (prefill)  [B, H_q, S_q, d]
+ *        q (decode_multi) [B, H_q, T_q, d]
  *        k, v cache   [B, H_kv, kv_cap, d] (position j of a sequence = row j)
  *        o            same shape as q, same dtype as q
- *        lse          [B, H_q] (decode) / [B, H_q, S_q] (prefill), float32
+ *        lse          [B, H_q] (decode) / [B, H_q, S_q] (prefill) /
+ *                     [B, H_q, T_q] (decode_multi), float32
  *  - Query head h reads KV head h / (H_q / H_kv): the G = H_q / H_kv query
  *    heads sharing a KV head are adjacent.
  *  - Q and K are already RoPE-rotated, V is raw, and for decode the new
@@ -111,7 +118,9 @@ size_t gqa_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int d,
  *   kv_lens  [B] int32, DEVICE memory: sequence b attends to its keys
  *            0 .. kv_lens[b]-1.  Contract (not checked): 1 <= kv_lens[b] <=
  *            max_kv_len.  Cache rows at or past kv_lens[b] are never read,
- *            so they may hold anything (NaN included).
+ *            so they may hold anything (NaN included).  A length above
+ *            max_kv_len is read as max_kv_len (nothing past it is read); a
+ *            length below 1 leaves that sequence's outputs undefined.
  *   o        [B, H_q, d]             dtype, written
  *   lse      [B, H_q] float32, written when non-NULL
  *   max_kv_len   host-side upper bound of kv_lens, <= kv_cap; it sizes the
@@ -155,6 +164,73 @@ int gqa_attn_decode_combine(const void* q, const void* k_cache,
                             int d, int kv_cap, int max_kv_len, float scale,
                             int dtype, int chunk_tokens, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * Multi-token decode: T_q new tokens per sequence (§3 running state of shape
+ * [G, T_q]; §5.2 M-fold of the G heads x T_q tokens into the GEMM rows;
+ * §0.5.3 q_block_meta {q_start, T_q}; §4 merge).
+ *
+ *   q        [B, H_q, T_q, d]        bf16: token t of each head is at
+ *            position kv_lens[b] - T_q + t of its sequence.
+ *   k_cache, v_cache [B, H_kv, kv_cap, d] bf16, read-only, already holding
+ *            the T_q new tokens' rows (precondition P4 of §0.5.1).
+ *   kv_lens  [B] int32, DEVICE memory: valid length L of each sequence,
+ *            new tokens included.  Token t sees keys 0 .. L - T_q + t (a
+ *            causal tail: the last T_q - 1 keys are hidden from the earlier
+ *            tokens).  Contract (not checked): T_q <= kv_lens[b] <=
+ *            max_kv_len.  A length above max_kv_len is read as max_kv_len;
+ *            rows of a sequence shorter than T_q get undefined values (no
+ *            memory outside the cache rows below max_kv_len is read).
+ *   o        [B, H_q, T_q, d] bf16, written
+ *   lse      [B, H_q, T_q] float32, written when non-NULL
+ *   max_kv_len, chunk_tokens, workspace: as for gqa_attn_decode, with the
+ *            sizes from the two functions below.
+ *
+ * Two kernel launches on `stream`.  Each workgroup of the first stages one
+ * split of one (sequence, KV head) through LDS and folds it into all G*T_q
+ * rows; the second is the decode combine over the B*H_q*T_q rows.
+ * Requirements: dtype == GQA_DTYPE_BF16, d == 128 and G*T_q <= 128 (else
+ * GQA_ERR_UNSUPPORTED); 1 <= T_q <= max_kv_len <= kv_cap (else
+ * GQA_ERR_INVALID_ARG).  T_q == 1 is plain decode (same results within
+ * rounding as gqa_attn_decode, through this kernel).
+ */
+int gqa_attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* kv_lens, void* o, float* lse, int B, int H_q,
+                          int H_kv, int d, int T_q, int kv_cap, int max_kv_len, float scale,
+                          int dtype, int chunk_tokens, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * Keys per multi-token decode split: `chunk_tokens` when positive (a
+ * multiple of 128), else the library's automatic choice.  Returns a negative
+ * gqa_status_t on invalid arguments (GQA_ERR_UNSUPPORTED for f32).
+ */
+int gqa_attn_decode_multi_split_tokens(int B, int H_kv, int T_q, int max_kv_len,
+                                       int chunk_tokens, int dtype);
+
+/*
+ * Device workspace (bytes) gqa_attn_decode_multi needs: one (m, l, O[d])
+ * float32 partial per (sequence, query head, token, split).  Returns 0 on
+ * invalid or unsupported arguments.
+ */
+size_t gqa_attn_decode_multi_workspace_bytes(int B, int H_q, int H_kv, int d, int T_q,
+                                             int max_kv_len, int chunk_tokens, int dtype);
+
+/*
+ * The two launches of gqa_attn_decode_multi separately (as
+ * gqa_attn_decode_partial / _combine are for decode): same arguments and
+ * validation; _partial then _combine on one stream is gqa_attn_decode_multi.
+ */
+int gqa_attn_decode_multi_partial(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* kv_lens, void* o, float* lse, int B,
+                                  int H_q, int H_kv, int d, int T_q, int kv_cap,
+                                  int max_kv_len, float scale, int dtype, int chunk_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+int gqa_attn_decode_multi_combine(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* kv_lens, void* o, float* lse, int B,
+                                  int H_q, int H_kv, int d, int T_q, int kv_cap,
+                                  int max_kv_len, float scale, int dtype, int chunk_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Prefill attention over a chunk of S_q queries (§5.4).

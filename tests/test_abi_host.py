@@ -132,3 +132,54 @@ def _prefill(**kw):
 ])
 def test_prefill_rejects_before_launch(kw, status):
     assert _prefill(**kw) == status
+
+
+def test_multi_split_and_workspace_rules():
+    L = binding.lib()
+    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 4, 32768, 0, BF16) == 1024
+    assert L.gqa_attn_decode_multi_split_tokens(4, 8, 4, 131072, 0, BF16) == 2048
+    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 4, 100, 0, BF16) == 128    # tiny context
+    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 4, 32768, 384, BF16) == 384
+    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 4, 32768, 200, BF16) == -INVALID
+    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 4, 32768, 0, F32) == -UNSUPPORTED
+    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 0, 32768, 0, BF16) == -INVALID
+    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 9, 8, 0, BF16) == -INVALID   # T_q > L
+    n = L.gqa_attn_decode_multi_workspace_bytes(1, 64, 8, 128, 4, 32768, 1024, BF16)
+    assert n >= 64 * 4 * 32 * (128 + 2) * 4
+    assert L.gqa_attn_decode_multi_workspace_bytes(1, 64, 8, 128, 17, 32768, 0, BF16) == 0
+    assert L.gqa_attn_decode_multi_workspace_bytes(1, 64, 8, 96, 4, 32768, 0, BF16) == 0
+
+
+def _decode_multi(fn="gqa_attn_decode_multi", **kw):
+    a = dict(q=P, k=P, v=P, lens=P, o=P2, lse=None, B=1, H_q=8, H_kv=1, d=128, T_q=4, cap=256,
+             maxlen=256, scale=0.088, dtype=BF16, chunk=0, ws=P2, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return getattr(binding.lib(), fn)(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"],
+                                         a["B"], a["H_q"], a["H_kv"], a["d"], a["T_q"],
+                                         a["cap"], a["maxlen"], a["scale"], a["dtype"],
+                                         a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID),
+    (dict(v=None), INVALID),
+    (dict(lens=None), INVALID),
+    (dict(o=ctypes.c_void_p(0x200004)), INVALID),        # misaligned
+    (dict(T_q=0), INVALID),
+    (dict(T_q=300, H_q=1), INVALID),                     # T_q > max_kv_len
+    (dict(maxlen=257), INVALID),                         # > kv_cap
+    (dict(H_kv=3), INVALID),
+    (dict(scale=float("-inf")), INVALID),
+    (dict(chunk=64), INVALID),
+    (dict(dtype=F32), UNSUPPORTED),
+    (dict(d=64), UNSUPPORTED),
+    (dict(T_q=17), UNSUPPORTED),                         # G * T_q > 128
+    (dict(H_q=64, H_kv=1, T_q=3), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x200008)), WORKSPACE),
+    (dict(wsb=1024), WORKSPACE),
+])
+@pytest.mark.parametrize("fn", ["gqa_attn_decode_multi", "gqa_attn_decode_multi_partial",
+                                "gqa_attn_decode_multi_combine"])
+def test_decode_multi_rejects_before_launch(kw, status, fn):
+    assert _decode_multi(fn, **kw) == status
