@@ -48,7 +48,8 @@ def parse():
                     help="run one entry point only (for profiler runs)")
     ap.add_argument("--chunk", type=int, default=0, help="decode keys per split (0 = auto)")
     ap.add_argument("--decode-workload", default="decode_llama70b_32k",
-                    help="decode workload name (the headline is decode_llama70b_32k)")
+                    help="decode workload name (the headline is decode_llama70b_32k; "
+                         "decode_multi_* workloads run gqa_attn_decode_multi)")
     ap.add_argument("--prefill-workload", default="prefill_causal_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -111,9 +112,10 @@ def cpu_baseline_decode(w, x_cpu, seconds):
     import oracle
     q, k, v = (x_cpu[n] for n in ("q", "k", "v"))
     lens = np.array(w.lens)
+    fn = oracle.decode_multi if w.kind == "decode_multi" else oracle.decode
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.decode(q, k, v, lens, w.scale)
+        fn(q, k, v, lens, w.scale)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1000:
@@ -121,7 +123,7 @@ def cpu_baseline_decode(w, x_cpu, seconds):
     gbs = w.decode_bytes() * reps / el / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle",
             "sample": f"{reps} full decode call(s) of {w.name} (B={w.B}, lens={list(w.lens)}, "
-                      f"all {w.H_q} heads) in {el:.1f} s, numpy fp64"}
+                      f"T_q={w.T_q}, all {w.H_q} heads) in {el:.1f} s, numpy fp64"}
 
 
 def cpu_baseline_prefill(w, x_cpu, seconds):
@@ -172,19 +174,27 @@ def main():
 
     wd = inputs.WORKLOADS[args.decode_workload]
     dec_dtype = gq.DTYPE_F32 if wd.dtype == "f32" else gq.DTYPE_BF16
+    multi = wd.kind == "decode_multi"
     wp = inputs.WORKLOADS[args.prefill_workload]
     do_dec = args.only in ("decode", "both")
     do_pre = args.only in ("prefill", "both")
 
     # ---- inputs, resident in HBM before timing
     if do_dec:
-        copies = [inputs.make_decode(wd, device=dev, seed=inputs.SEEDS[wd.name] + 100 * i)
+        make = inputs.make_decode_multi if multi else inputs.make_decode
+        copies = [make(wd, device=dev, seed=inputs.SEEDS[wd.name] + 100 * i)
                   for i in range(max(1, args.kv_copies))]
-        need = gq.decode_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.max_kv_len, args.chunk,
-                                         dec_dtype)
+        if multi:
+            need = gq.decode_multi_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.T_q,
+                                                   wd.max_kv_len, args.chunk, dec_dtype)
+            chunk = gq.decode_multi_split_tokens(wd.B, wd.H_kv, wd.T_q, wd.max_kv_len,
+                                                 args.chunk, dec_dtype)
+        else:
+            need = gq.decode_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.max_kv_len,
+                                             args.chunk, dec_dtype)
+            chunk = gq.decode_split_tokens(wd.B, wd.H_kv, wd.max_kv_len, args.chunk, dec_dtype)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         o_dec = torch.empty_like(copies[0]["q"])
-        chunk = gq.decode_split_tokens(wd.B, wd.H_kv, wd.max_kv_len, args.chunk, dec_dtype)
     if do_pre:
         xp = inputs.make_prefill(wp, device=dev)
         o_pre = torch.empty_like(xp["q"])
@@ -196,9 +206,10 @@ def main():
 
     def decode_call(i, phase="both"):
         x = copies[i % len(copies)]
-        gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=wd.max_kv_len,
-                  scale=wd.scale, chunk_tokens=args.chunk, out=o_dec, workspace=ws,
-                  stream=stream, phase=phase)
+        fn = gq.decode_multi if multi else gq.decode
+        fn(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=wd.max_kv_len,
+           scale=wd.scale, chunk_tokens=args.chunk, out=o_dec, workspace=ws,
+           stream=stream, phase=phase)
 
     for i in range(args.warmup):
         if do_dec:
@@ -264,6 +275,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": " + ".join(n for n, on in ((wd.name, do_dec), (wp.name, do_pre)) if on),
                    "decode": {"B": wd.B, "H_q": wd.H_q, "H_kv": wd.H_kv, "d": wd.d,
+                              "T_q": wd.T_q, "entry_point": "gqa_attn_decode_multi" if multi
+                              else "gqa_attn_decode",
                               "kv_lens": list(wd.lens), "kv_copies": len(copies) if do_dec else 0,
                               "keys_per_split": chunk if do_dec else None},
                    "prefill": {"B": wp.B, "H_q": wp.H_q, "H_kv": wp.H_kv, "d": wp.d,
@@ -275,7 +288,7 @@ def main():
         t_s = dec_b2b_us / 1e6
         gbs = wd.decode_bytes() / t_s / 1e9
         # Split kernel's algorithmic bytes: K and V of the valid keys plus Q.
-        part_bytes = wd.kv_bytes() + wd.B * wd.H_q * wd.d * wd.elem_bytes
+        part_bytes = wd.kv_bytes() + wd.B * wd.H_q * wd.T_q * wd.d * wd.elem_bytes
         part_gbs = part_bytes / (part_us / 1e6) / 1e9
         out["value"] = round(gbs, 2)
         out["decode"] = {"us_per_call_back_to_back": round(dec_b2b_us, 3),
@@ -284,10 +297,20 @@ def main():
                          "GB_s": round(gbs, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                          "bytes_per_call": wd.decode_bytes(),
                          "partial_kernel_us_mean": round(part_us, 3)}
-        out["roofline"] = {"bound": "hbm", "kernel": f"decode_partial_{wd.dtype}_kernel",
+        if multi:
+            rows = wd.G * wd.T_q
+            rgroups = 1 if rows <= 32 else (2 if rows <= 64 else 4)
+            kname, tkey = f"decode_multi_partial_kernel<{rgroups}>", "decode_multi_partial"
+            tf = wd.decode_multi_flops() / t_s / 1e12
+            out["decode"].update({"flops_per_call": wd.decode_multi_flops(),
+                                  "TFLOP_s": round(tf, 3),
+                                  "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)})
+        else:
+            kname, tkey = f"decode_partial_{wd.dtype}_kernel", "decode_partial"
+        out["roofline"] = {"bound": "hbm", "kernel": kname,
                            "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(part_gbs / HBM_PEAK_GBS, 4),
-                           "traffic": traffic_from_profiles("decode_partial", wd.name),
+                           "traffic": traffic_from_profiles(tkey, wd.name),
                            "algorithmic_bytes_per_launch": part_bytes,
                            "launch_us_mean": round(part_us, 3)}
     if do_pre:

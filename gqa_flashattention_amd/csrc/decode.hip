@@ -383,53 +383,87 @@ struct MergeAcc {
   float lacc;
 };
 
-__device__ __forceinline__ void merge_group(MergeAcc& st, const float* ml, const float* po,
-                                            int s0, int s1, int stride) {
-  constexpr int kGroup = 16;
-  float mv[kGroup], lv[kGroup];
-  f32x4 ov[kGroup];
+constexpr int kMergeGroup = 16;
+
+struct MergeLoads {
+  float m[kMergeGroup], l[kMergeGroup];
+  f32x4 o[kMergeGroup];
+};
+
+// Loads splits s0, s0 + stride, ...; indices at or past `s_alloc` (the
+// partials the workspace holds per row) re-read the last one, so every load
+// is unconditional and all of them are in flight together.  Such splits lie
+// past the sequence's split count and are discarded by merge_fold.
+__device__ __forceinline__ void merge_load(MergeLoads& g, const float* ml, const float* po, int s0,
+                                           int s_alloc, int stride) {
 #pragma unroll
-  for (int u = 0; u < kGroup; ++u) {
-    const int s = s0 + u * stride;
-    const bool ok = s < s1;
-    const f32x2 m2 = ok ? *reinterpret_cast<const f32x2*>(ml + 2 * s) : f32x2{kNegInf, 0.f};
-    ov[u] = ok ? *reinterpret_cast<const f32x4*>(po + (size_t)s * kD) : f32x4{0.f, 0.f, 0.f, 0.f};
-    mv[u] = m2[0];
-    lv[u] = m2[1];
+  for (int u = 0; u < kMergeGroup; ++u) {
+    const int s = min(s0 + u * stride, s_alloc - 1);
+    const f32x2 m2 = *reinterpret_cast<const f32x2*>(ml + 2 * s);
+    g.o[u] = *reinterpret_cast<const f32x4*>(po + (size_t)s * kD);
+    g.m[u] = m2[0];
+    g.l[u] = m2[1];
+  }
+}
+
+// Folds the loaded splits below `s_valid` (the splits of this call) into
+// `st`; the others are replaced by the identity (-inf, 0, 0) before use.
+__device__ __forceinline__ void merge_fold(MergeAcc& st, MergeLoads& g, int s0, int s_valid,
+                                           int stride) {
+#pragma unroll
+  for (int u = 0; u < kMergeGroup; ++u) {
+    if (s0 + u * stride >= s_valid) {
+      g.m[u] = kNegInf;
+      g.l[u] = 0.f;
+      g.o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
   float gm = st.M;
 #pragma unroll
-  for (int u = 0; u < kGroup; ++u) gm = fmaxf(gm, mv[u]);
-  if (gm == kNegInf) return;
-  const float c = fast_exp2(st.M - gm);
+  for (int u = 0; u < kMergeGroup; ++u) gm = fmaxf(gm, g.m[u]);
+  // Branch-free (so that no load is sunk behind a branch): with every side
+  // empty, gm = -inf and the weights below are exp2(-inf) = 0.
+  const float ref = gm == kNegInf ? 0.f : gm;
+  const float c = fast_exp2(st.M - ref);
   st.acc *= c;
   st.lacc *= c;
 #pragma unroll
-  for (int u = 0; u < kGroup; ++u) {
-    const float w = fast_exp2(mv[u] - gm);
-    st.acc += w * ov[u];
-    st.lacc += w * lv[u];
+  for (int u = 0; u < kMergeGroup; ++u) {
+    const float w = fast_exp2(g.m[u] - ref);
+    st.acc += w * g.o[u];
+    st.lacc += w * g.l[u];
   }
   st.M = gm;
 }
 
-// Combine: one workgroup of 128 threads per (sequence, query head, token); 4 groups
-// of 32 threads take every 4th split, thread t covers output columns
+// Combine: one workgroup of 128 threads per (sequence, query head, token); 4
+// groups of 32 threads take every 4th split, thread t covers output columns
 // 4*(t%32) .. +4, and the groups merge through LDS.  Normalises once and
-// rounds to the output dtype (the final O / l of §4).
+// rounds to the output dtype (the final O / l of §4).  The first 64 splits'
+// loads are issued together with the sequence length's, so a call of up to
+// 64 splits costs one memory round trip; splits past the sequence's count
+// are discarded after the loads.
 template <typename OutT>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_combine_kernel(DecodeParams p) {
   const int bh = blockIdx.x;                 // folded row (sequence, head, token)
   const int b = bh / (p.H_q * p.T_q);
   const int t = threadIdx.x;
   const int grp = t >> 5;
   const int d0 = (t & 31) * 4;
-  const int L = min(p.kv_lens[b], p.max_kv_len);
-  const int ns = (L + p.chunk - 1) / p.chunk;
   const size_t part0 = (size_t)bh * p.n_split_max;
+  const float* ml = p.ws_ml + 2 * part0;
+  const float* po = p.ws_o + part0 * kD + d0;
+  const int len = p.kv_lens[b];
+  MergeLoads g;
+  merge_load(g, ml, po, grp, p.n_split_max, 4);
+  const int L = min(len, p.max_kv_len);
+  const int ns = (L + p.chunk - 1) / p.chunk;
   MergeAcc st{kNegInf, {0.f, 0.f, 0.f, 0.f}, 0.f};
-  for (int s0 = grp; s0 < ns; s0 += 64)
-    merge_group(st, p.ws_ml + 2 * part0, p.ws_o + part0 * kD + d0, s0, ns, 4);
+  merge_fold(st, g, grp, ns, 4);
+  for (int s0 = grp + 4 * kMergeGroup; s0 < ns; s0 += 4 * kMergeGroup) {
+    merge_load(g, ml, po, s0, p.n_split_max, 4);
+    merge_fold(st, g, s0, ns, 4);
+  }
   __shared__ float sm[4], sl[4];
   __shared__ f32x4 so[4][32];
   if ((t & 31) == 0) { sm[grp] = st.M; sl[grp] = st.lacc; }
@@ -439,10 +473,10 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
     float MM = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
     float l = 0.f;
-    for (int g = 0; g < 4; ++g) {
-      const float w = sm[g] == kNegInf ? 0.f : fast_exp2(sm[g] - MM);
-      a += w * so[g][t];
-      l += w * sl[g];
+    for (int g2 = 0; g2 < 4; ++g2) {
+      const float w = sm[g2] == kNegInf ? 0.f : fast_exp2(sm[g2] - MM);
+      a += w * so[g2][t];
+      l += w * sl[g2];
     }
     const float inv = 1.f / l;
     OutT* o = static_cast<OutT*>(p.o) + (size_t)bh * kD + d0;
