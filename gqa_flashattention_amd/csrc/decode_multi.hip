@@ -12,12 +12,12 @@
 // L - T_q, so token t sees keys j <= L - T_q + t) and §4 (unnormalised
 // (m, l, O) partials merged by log-sum-exp).
 //
-// GPU mapping.  One workgroup = 4 waves = one contiguous split of one
+// GPU mapping.  One workgroup = W waves = one contiguous split of one
 // (sequence, KV head).  The M = G*T_q folded rows (row r = token r % T_q of
 // head r / T_q, the memory order of q) form R = 1, 2 or 4 groups of 32;
-// wave w takes row group w % R and key slot w / R, so the 4 waves cover
-// R row groups x 4/R key slots.  A step stages 32 keys per key slot of K and
-// V in LDS (direct global -> LDS loads into a ring of steps, shared by the
+// wave w takes row group w % R and key slot w / R, so the W waves cover
+// R row groups x W/R key slots.  A step stages 32 keys per key slot of K and
+// V in LDS (direct global -> LDS loads into a ring of N steps, shared by the
 // waves of different row groups) and each wave folds its 32 keys into its
 // 32 rows:
 //   S^T = K . Q^T on the 32x32x16 bf16 MFMA (keys in M, rows in N), so a
@@ -25,6 +25,11 @@
 //   P = exp2(S*scale - ref) rounded to bf16 is directly the B operand of
 //   O^T = V^T . P^T, whose V^T operand comes from the row-major V tile
 //   through the transposing LDS read.
+// The waves meet at a barrier every step, so they would all run their
+// matrix work and their exponentials at the same time; instead each wave
+// issues the P.V of step s-1 between the exponentials of step s, keeping
+// the matrix unit busy while the vector ALUs work.  V of step s-1 therefore
+// stays in LDS through step s and the loads run N-2 steps ahead.
 // Softmax statistics use the lazy reference of the prefill kernel: weights
 // are taken relative to a per-row reference that moves only when a score
 // exceeds it by more than 64 (log2 units), detected by the lane sum of the
@@ -47,8 +52,6 @@ namespace gqa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kSub = 32;               // keys per wave per step
 constexpr int kRowBytes = kD * 2;      // one bf16 K or V row
 
@@ -59,16 +62,55 @@ constexpr float kRefBelow = 32.f;
 template <int N>
 using Int = std::integral_constant<int, N>;
 
-// Geometry for R row groups of 32.
-template <int R>
+// f(Int<0>), f(Int<1>), ..., f(Int<N-1>).
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>());
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
+// Geometry for R row groups of 32, W waves per workgroup and a ring of N
+// steps in LDS.
+template <int R, int W, int N>
 struct MqShape {
-  static constexpr int kSlots = kWaves / R;               // key slots
-  static constexpr int kStep = kSub * kSlots;             // keys per step (128, 64, 32)
+  static constexpr int kWaves = W;
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kSlots = W / R;                    // key slots
+  static constexpr int kStep = kSub * kSlots;             // keys per step
   static constexpr int kStepBytes = kStep * kRowBytes;    // K (or V) bytes of one step
-  static constexpr int kRing = R == 4 ? 3 : 2;            // steps resident in LDS
-  static constexpr int kInsts = kStep / 4 / kWaves;       // 1 KiB loads per wave per step, K or V
-  static constexpr int kOcc = R == 1 ? 1 : 2;             // workgroups per CU (LDS bound for R = 1)
+  static constexpr int kRing = N;                         // steps resident in LDS
+  static constexpr int kInsts = kStep / 4 / W;            // 1 KiB loads per wave per step, K or V
+  static_assert(W % R == 0 && kInsts * 4 * W == kStep, "shape");
+  static_assert(2 * N * kStepBytes <= 128 * 1024, "LDS");
+  static_assert(N >= 3 && 2 * kInsts * (N - 3) <= 63, "vmcnt");
 };
+
+// Launch shape per row-group count: waves per workgroup and ring depth
+// (measured on MI355X against 1-8 waves and 3-8 steps; the time barely
+// moves, these are the best):
+//   R = 1: 2 waves, 64-key steps, 4 steps in LDS (two 32 KiB steps in flight)
+//   R = 2: 4 waves, 64-key steps, 4 steps
+//   R = 4: 8 waves (two per SIMD), 64-key steps, 4 steps
+template <int R> struct MqLaunch;
+template <> struct MqLaunch<1> { using S = MqShape<1, 2, 4>; };
+template <> struct MqLaunch<2> { using S = MqShape<2, 4, 4>; };
+template <> struct MqLaunch<4> { using S = MqShape<4, 8, 4>; };
+
+// s_waitcnt leaving `ahead` (0..A) steps of `kPer` loads each in flight.
+template <int kPer, int A>
+__device__ __forceinline__ void wait_vm_steps(int ahead) {
+  if constexpr (A == 0) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  } else {
+    if (ahead >= A) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(A * kPer));
+    } else {
+      wait_vm_steps<kPer, A - 1>(ahead);
+    }
+  }
+}
 
 // LDS block of one wave's row-group state for the merge of key slots:
 // 32 rows x (128 O + m + l + 2 pad) floats.
@@ -77,11 +119,11 @@ constexpr int kRedFloats = 32 * kRedStride;
 
 }  // namespace
 
-// Grid: (n_split_max, H_kv, B); block: 256 threads.
+// Grid: (n_split_max, H_kv, B); block: 64 * W threads.
 template <int R>
-__global__ __launch_bounds__(kThreads, MqShape<R>::kOcc) void decode_multi_partial_kernel(
+__global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_partial_kernel(
     DecodeParams p) {
-  using S = MqShape<R>;
+  using S = typename MqLaunch<R>::S;
   // K ring then V ring, contiguous so that the merge can reuse both.
   __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][S::kRing][S::kStep * kD];
 
@@ -166,7 +208,7 @@ __global__ __launch_bounds__(kThreads, MqShape<R>::kOcc) void decode_multi_parti
     ld_off[0][i] = r * kRowBytes + 16 * k_swz(r, lane & 15);   // XOR is an involution
     ld_off[1][i] = r * kRowBytes + 16 * v_swz(r, lane & 15);
   }
-  auto load_step = [&](auto slot_c, int s) {
+  auto load_step = [&](auto slot_c, int s) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
     const int key0 = start + s * S::kStep;
     const unsigned bytes = (unsigned)(end - key0) * kRowBytes;
@@ -194,7 +236,7 @@ __global__ __launch_bounds__(kThreads, MqShape<R>::kOcc) void decode_multi_parti
   // P = exp2(S*scale - ref) of the lane's 16 scores, rounded to bf16 in the
   // P^T operand layout (key step st: keys 16*st + {0..3, 8..11} + 4*h2);
   // returns their fp32 sum.
-  auto exps = [&](const f32x16& sacc, float negr, u32x4 (&pw)[2]) -> float {
+  auto exps = [&](const f32x16& sacc, float negr, u32x4 (&pw)[2]) __attribute__((always_inline)) -> float {
     float psum = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -208,17 +250,47 @@ __global__ __launch_bounds__(kThreads, MqShape<R>::kOcc) void decode_multi_parti
     return psum;
   };
 
-  // Step s: scores of this wave's 32 keys against its 32 rows, the tail
-  // mask (last steps only), the softmax against the reference, and P.V.
-  auto compute = [&](auto slot_c, int s) {
+  // O^T += V^T . P^T of one step from ring slot `slot` (8 MFMAs).  The V
+  // operand reads are issued first, then the MFMAs.
+  auto pv_reads = [&](auto slot_c, bf16x8 (&va)[8]) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const unsigned a = vaddr[dt] + slot * S::kStepBytes + 4096 * st;
+        const u32x2 w0 = __builtin_bit_cast(u32x2, lds_read_tr16(a));
+        const u32x2 w1 = __builtin_bit_cast(u32x2, lds_read_tr16(a + 8 * kRowBytes));
+        const u32x4 av = {w0[0], w0[1], w1[0], w1[1]};
+        va[4 * st + dt] = as_bf16x8(av);
+      }
+  };
+
+  // Step s: scores of this wave's 32 keys against its 32 rows (S MFMAs),
+  // the tail mask (last steps only), then the softmax of step s issued
+  // between the 8 MFMAs of the previous step's P.V (`pprev`, V from slot
+  // `pslot`), so that the matrix unit works while the vector ALUs compute
+  // the exponentials.  P of step s is left in `pprev` for the next step.
+  u32x4 pprev[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+  auto compute = [&](auto slot_c, auto pslot_c, int s) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
+    // All eight K operand reads are issued before the first MFMA (one LDS
+    // round trip per step instead of eight).
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 ka[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) ka[kk] = *lds_ptr<bf16x8>(kaddr[kk] + slot * S::kStepBytes);
     f32x16 sacc;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 a = *lds_ptr<bf16x8>(kaddr[kk] + slot * S::kStepBytes);
       const f32x16 zero = {};
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kk], kk ? sacc : zero, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qb[kk], kk ? sacc : zero, 0, 0, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 K reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // then the 8 S MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 va[8];
+    pv_reads(pslot_c, va);
     if (s >= n_full) {
       const int key0 = start + s * S::kStep + 32 * kq;
 #pragma unroll
@@ -227,13 +299,31 @@ __global__ __launch_bounds__(kThreads, MqShape<R>::kOcc) void decode_multi_parti
         if (key > vis_last) sacc[i] = kNegInf;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // Softmax of step s against the reference, one exponential pair per
+    // P.V MFMA of step s-1.
+    const float negr = -m_ref;
     u32x4 pw[2];
-    float psum = exps(sacc, -m_ref, pw);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], as_bf16x8(pprev[i >> 2]), o[i & 3],
+                                                         0, 0, 0);
+      const int st = i >> 2, jj = i & 3;
+      const float e0 = fast_exp2(__builtin_fmaf(sacc[8 * st + 2 * jj], sl2, negr));
+      const float e1 = fast_exp2(__builtin_fmaf(sacc[8 * st + 2 * jj + 1], sl2, negr));
+      psum += e0 + e1;
+      pw[st][jj] = pack_bf16x2(e0, e1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // then the pair's VALU work
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (__any(!(psum <= kPsumLimit))) {
       // Some weight exceeds 2^64 (a score more than 64 above the reference,
       // always so on a row's first visible keys): move the reference of
-      // such rows to 32 below their max, rescale O and l, redo P.  A row
-      // with no visible key yet keeps the reference -inf and gets P = 0.
+      // such rows to 32 below their max, rescale O (which now holds steps
+      // up to s-1) and l, redo P.  A row with no visible key yet keeps the
+      // reference -inf and gets P = 0.
       float hmax = kNegInf;
 #pragma unroll
       for (int i = 0; i < 16; ++i) hmax = fmaxf(hmax, sacc[i]);
@@ -247,47 +337,65 @@ __global__ __launch_bounds__(kThreads, MqShape<R>::kOcc) void decode_multi_parti
       psum = exps(sacc, m_ref == kNegInf ? 0.f : -m_ref, pw);
     }
     lpart += psum;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const bf16x8 pb = as_bf16x8(pw[st]);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const unsigned a = vaddr[dt] + slot * S::kStepBytes + 4096 * st;
-        const u32x2 w0 = __builtin_bit_cast(u32x2, lds_read_tr16(a));
-        const u32x2 w1 = __builtin_bit_cast(u32x2, lds_read_tr16(a + 8 * kRowBytes));
-        const u32x4 av = {w0[0], w0[1], w1[0], w1[1]};
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), pb, o[dt], 0, 0, 0);
-      }
-    }
+    pprev[0] = pw[0];
+    pprev[1] = pw[1];
   };
 
-  // Ring schedule: steps 0 .. kRing-2 are loaded up front; step s waits for
-  // its own loads (leaving later steps' loads in flight), meets the other
-  // waves at a barrier (their loads of step s have landed, and all are done
-  // with step s-1, whose slot is refilled next), issues the load of step
-  // s + kRing - 1 and computes.
-  auto step = [&](auto slot_c, int s) {
+  // Ring schedule.  Step s reads K of step s and V of step s-1, so slot
+  // (s-1) % N is free only after step s; the loads run N-2 steps ahead.
+  // Steps 0 .. N-3 are loaded up front.  Step s waits for its own loads
+  // (leaving the later steps' loads in flight), meets the other waves at a
+  // barrier (their loads of step s have landed, and all are done with step
+  // s-1, the last reader of slot (s-2) % N), issues the load of step
+  // s + N - 2 into that slot and computes.  The first step's P.V reads the
+  // V slot N-1 with P = 0; that slot is zeroed so that no stale bit pattern
+  // (a NaN) meets the zero weights.
+  constexpr int kPer = 2 * S::kInsts;   // load instructions per wave per step
+  auto wait_step = [&](int s) __attribute__((always_inline)) {
+    const int ahead = min(S::kRing - 3, nsteps - 1 - s);   // later steps already issued
+    wait_vm_steps<kPer, S::kRing - 3>(ahead);
+  };
+  auto step = [&](auto slot_c, int s) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
-    if (S::kRing == 3 && s + 1 < nsteps) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::kInsts));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
+    wait_step(s);
     __syncthreads();
-    if (s + S::kRing - 1 < nsteps) load_step(Int<(slot + S::kRing - 1) % S::kRing>(), s + S::kRing - 1);
-    compute(slot_c, s);
+    if (s + S::kRing - 2 < nsteps) load_step(Int<(slot + S::kRing - 2) % S::kRing>(), s + S::kRing - 2);
+    compute(slot_c, Int<(slot + S::kRing - 1) % S::kRing>(), s);
   };
 
-  load_step(Int<0>(), 0);
-  if (S::kRing == 3 && nsteps > 1) load_step(Int<1 % S::kRing>(), 1);
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(&sKV[1][S::kRing - 1][0]);
+    for (int i = t; i < S::kStep * kD / 8; i += S::kThreads) z[i] = u32x4{0, 0, 0, 0};
+  }
+  // Prologue loads, then the steps in groups of N so that ring slots are
+  // compile-time constants, then the remaining steps, then the last P.V.
+  static_for<S::kRing - 2>([&](auto i_c) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_c)::value;
+    if (i < nsteps) load_step(Int<i>(), i);
+  });
   int s = 0;
   for (; s + S::kRing <= nsteps; s += S::kRing) {
-    step(Int<0>(), s);
-    step(Int<1>(), s + 1);
-    if constexpr (S::kRing == 3) step(Int<2 % S::kRing>(), s + 2);
+    static_for<S::kRing>([&](auto i_c) __attribute__((always_inline)) {
+      step(i_c, s + decltype(i_c)::value);
+    });
   }
-  if (s < nsteps) step(Int<0>(), s);
-  if (S::kRing == 3 && s + 1 < nsteps) step(Int<1>(), s + 1);
+  static_for<S::kRing - 1>([&](auto i_c) __attribute__((always_inline)) {
+    if (s + decltype(i_c)::value < nsteps) step(i_c, s + decltype(i_c)::value);
+  });
+  {
+    // P.V of the last step, whose V is in slot (nsteps - 1) % N.
+    const int last = (nsteps - 1) % S::kRing;
+    static_for<S::kRing>([&](auto i_c) __attribute__((always_inline)) {
+      if (decltype(i_c)::value == last) {
+        bf16x8 va[8];
+        pv_reads(i_c, va);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], as_bf16x8(pprev[i >> 2]),
+                                                             o[i & 3], 0, 0, 0);
+      }
+    });
+  }
 
   // Row sums over both halves; merge the key slots of each row group.
   const float lrow = lpart + __shfl_xor(lpart, 32, 64);
@@ -367,13 +475,16 @@ hipError_t launch_decode_multi(const DecodeParams& p, hipStream_t stream, int ph
     const dim3 grid(p.n_split_max, p.H_kv, p.B);
     switch (decode_multi_row_groups(p.G * p.T_q)) {
       case 1:
-        hipLaunchKernelGGL(decode_multi_partial_kernel<1>, grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL(decode_multi_partial_kernel<1>, grid, dim3(MqLaunch<1>::S::kThreads), 0,
+                           stream, p);
         break;
       case 2:
-        hipLaunchKernelGGL(decode_multi_partial_kernel<2>, grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL(decode_multi_partial_kernel<2>, grid, dim3(MqLaunch<2>::S::kThreads), 0,
+                           stream, p);
         break;
       default:
-        hipLaunchKernelGGL(decode_multi_partial_kernel<4>, grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL(decode_multi_partial_kernel<4>, grid, dim3(MqLaunch<4>::S::kThreads), 0,
+                           stream, p);
         break;
     }
     const hipError_t e = hipGetLastError();
