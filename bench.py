@@ -76,9 +76,9 @@ def calibrate_copy():
 
 def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` on `workload` from the committed
-    counter summary, if it was taken on the current kernel source; otherwise
-    None."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_decode_llama70b_32k_prefill_causal_8k.md")
+    counter summary (calibrated FETCH_SIZE + WRITE_SIZE), if it was taken on
+    the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "all_workloads_kernel_stats_and_counters.md")
     if not os.path.exists(path):
         return None
     import hashlib
@@ -86,9 +86,8 @@ def traffic_from_profiles(kernel: str, workload: str):
     m = re.search(r"```json\n(.*?)\n```", text, re.S)
     if not m:
         return None
-    table = json.loads(m.group(1))
-    ent = table.get(kernel)
-    if not ent or ent.get("workload") != workload:
+    ent = json.loads(m.group(1)).get(f"{kernel}@{workload}")
+    if not ent:
         return None
     src = os.path.join(ROOT, "gqa_flashattention_amd", "csrc", ent["source"])
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
