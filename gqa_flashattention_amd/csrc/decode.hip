@@ -48,27 +48,28 @@ struct Block {
   u32x4 v[8];
 };
 
-template <bool kGuard>
-__device__ __forceinline__ void load_block(Block& blk, const __bf16* kbase, const __bf16* vbase,
-                                           int key0, int kend, int lane) {
-  const int r = lane & 15;
-  const int g = lane >> 4;
+// Per-lane byte offsets of a block's loads relative to the block's first
+// key; the block's own offset goes in the scalar offset of the load.
+struct BlockOffsets {
+  int k[2];   // K row l%16 (+16 rows for sb = 1), d = 8*(l/16)
+  int v[2];   // V row 4*(l/16) (+16 rows for j >= 4), d = 8*(l%16)
+};
+
+// The wave's K and V rows go through buffer resources that end at the
+// wave's last key: rows past it read as zeros without touching memory, so
+// a partial last block needs no guarded loads (its keys are masked, and its
+// zero V rows meet zero weights).  Nontemporal: each byte is read once.
+__device__ __forceinline__ void load_block(Block& blk, __amdgpu_buffer_rsrc_t rk,
+                                           __amdgpu_buffer_rsrc_t rv, const BlockOffsets& off,
+                                           int soff) {
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    const int key = key0 + 16 * sb + r;
-    const bool ok = !kGuard || key < kend;
-    const __bf16* row = kbase + (size_t)key * kD + 8 * g;
+  for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      blk.k[sb][kb] = ok ? ld16_stream(row + 32 * kb) : u32x4{0, 0, 0, 0};
-    }
-  }
+    for (int kb = 0; kb < 4; ++kb)
+      blk.k[sb][kb] = __builtin_amdgcn_raw_buffer_load_b128(rk, off.k[sb] + 64 * kb, soff, 2);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int key = key0 + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
-    const bool ok = !kGuard || key < kend;
-    blk.v[j] = ok ? ld16_stream(vbase + (size_t)key * kD + 8 * r) : u32x4{0, 0, 0, 0};
-  }
+  for (int j = 0; j < 8; ++j)
+    blk.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, off.v[j >> 2] + (j & 3) * kD * 2, soff, 2);
 }
 
 // Running state of one wave: query n = lane % 16 (rows >= G are padding).
@@ -78,9 +79,11 @@ struct State {
   f32x4 o[8];    // O^T, d-tile dt: lane holds d = 8*(4*(lane/16)+i) + dt, query n
 };
 
-template <bool kGuard>
+// `masked` (wave-uniform) is set for the wave's last block when it is
+// partial: keys at or past `kend` get weight 0.
 __device__ __forceinline__ void fold_block(State& st, const Block& blk, const bf16x8 (&qb)[4],
-                                           int key0, int kend, float scale_log2, int lane) {
+                                           int key0, int kend, float scale_log2, int lane,
+                                           bool masked) {
   const int g = lane >> 4;
   // S^T = K . Q^T for two 16-key sub-blocks.
   f32x4 s[2];
@@ -91,18 +94,21 @@ __device__ __forceinline__ void fold_block(State& st, const Block& blk, const bf
     for (int kb = 0; kb < 4; ++kb)
       s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(blk.k[sb][kb]), qb[kb], s[sb], 0, 0, 0);
   }
-  // Scale into the log2 domain; mask keys past the end (guarded block only).
+  // Scale into the log2 domain; mask keys past the end (partial block only).
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) s[sb] *= scale_log2;
+  if (masked) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (key0 + 16 * sb + 4 * g + i >= kend) s[sb][i] = kNegInf;
+  }
   float bmax = kNegInf;
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
+  for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = s[sb][i] * scale_log2;
-      if (kGuard && key0 + 16 * sb + 4 * g + i >= kend) x = kNegInf;
-      s[sb][i] = x;
-      bmax = fmaxf(bmax, x);
-    }
-  }
+    for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[sb][i]);
   bmax = wave_max_xor(bmax, 16);
   bmax = wave_max_xor(bmax, 32);
   const float m_new = fmaxf(st.m, bmax);
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
   const int start = split * p.chunk;
   if (start >= L) return;
   const int end = min(start + p.chunk, L);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int lane = threadIdx.x & 63;
   const int quarter = p.chunk / kWaves;
   const int ws = start + wave * quarter;
@@ -180,17 +186,26 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
   if (ws < we) {
     // Two register buffers, A and B, alternate so that the next block's
     // loads are in flight while the current block is folded.  Only the
-    // last block of the sequence can be partial (guarded).
+    // last block of the wave's range can be partial (masked).
     const int nblk = (we - ws + kBlk - 1) / kBlk;
     const bool tail = (we - ws) % kBlk != 0;
+    const unsigned bytes = (unsigned)(we - ws) * (kD * 2);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (size_t)ws * kD), (short)0, bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (size_t)ws * kD), (short)0, bytes, 0x00020000);
+    BlockOffsets off;
+    {
+      const int r = lane & 15;
+      off.k[0] = r * (kD * 2) + 16 * g;
+      off.k[1] = off.k[0] + 16 * (kD * 2);
+      off.v[0] = 4 * g * (kD * 2) + 16 * r;
+      off.v[1] = off.v[0] + 16 * (kD * 2);
+    }
     Block A, B;
-    auto load_i = [&](Block& bl, int i) {
-      if (tail && i == nblk - 1) load_block<true>(bl, kbase, vbase, ws + i * kBlk, we, lane);
-      else load_block<false>(bl, kbase, vbase, ws + i * kBlk, we, lane);
-    };
+    auto load_i = [&](Block& bl, int i) { load_block(bl, rk, rv, off, i * kBlk * kD * 2); };
     auto fold_i = [&](const Block& bl, int i) {
-      if (tail && i == nblk - 1) fold_block<true>(st, bl, qb, ws + i * kBlk, we, p.scale_log2, lane);
-      else fold_block<false>(st, bl, qb, ws + i * kBlk, we, p.scale_log2, lane);
+      fold_block(st, bl, qb, ws + i * kBlk, we, p.scale_log2, lane, tail && i == nblk - 1);
     };
     load_i(A, 0);
     for (int i = 0; i < nblk; i += 2) {
