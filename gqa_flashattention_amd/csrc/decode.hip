@@ -139,7 +139,9 @@ __device__ __forceinline__ void fold_block(State& st, const Block& blk, const bf
     for (int jj = 0; jj < 4; ++jj) {
       const unsigned int lo = blk.v[2 * jj][w];
       const unsigned int hi = blk.v[2 * jj + 1][w];
-      a[jj] = (dt & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      // One byte permute: the low (dt even) or high (dt odd) halves of
+      // lo and hi, lo's in the low half of the result.
+      a[jj] = __builtin_amdgcn_perm(hi, lo, (dt & 1) ? 0x07060302u : 0x05040100u);
     }
     st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pb, st.o[dt], 0, 0, 0);
   }
