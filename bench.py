@@ -186,7 +186,7 @@ def main():
         if multi:
             need = gq.decode_multi_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.T_q,
                                                    wd.max_kv_len, args.chunk, dec_dtype)
-            chunk = gq.decode_multi_split_tokens(wd.B, wd.H_kv, wd.T_q, wd.max_kv_len,
+            chunk = gq.decode_multi_split_tokens(wd.B, wd.H_q, wd.H_kv, wd.T_q, wd.max_kv_len,
                                                  args.chunk, dec_dtype)
         else:
             need = gq.decode_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.max_kv_len,
@@ -296,7 +296,7 @@ def main():
                          "GB_s": round(gbs, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                          "bytes_per_call": wd.decode_bytes(),
                          "partial_kernel_us_mean": round(part_us, 3)}
-        if multi:
+        if multi and wd.G * wd.T_q > 16:
             rows = wd.G * wd.T_q
             rgroups = 1 if rows <= 32 else (2 if rows <= 64 else 4)
             kname, tkey = f"decode_multi_partial_kernel<{rgroups}>", "decode_multi_partial"

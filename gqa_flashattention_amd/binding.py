@@ -38,7 +38,7 @@ SIGNATURES = {
                                      _i, _i, _vp, _sz, _vp]),
     "gqa_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                               _f, _i, _vp]),
-    "gqa_attn_decode_multi_split_tokens": (_i, [_i, _i, _i, _i, _i, _i]),
+    "gqa_attn_decode_multi_split_tokens": (_i, [_i, _i, _i, _i, _i, _i, _i]),
     "gqa_attn_decode_multi_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "gqa_attn_decode_multi": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                                    _i, _i, _vp, _sz, _vp]),
@@ -155,8 +155,10 @@ def decode(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chunk_toke
     return (out, lse) if return_lse else out
 
 
-def decode_multi_split_tokens(B, H_kv, T_q, max_kv_len, chunk_tokens=0, dtype=DTYPE_BF16) -> int:
-    r = lib().gqa_attn_decode_multi_split_tokens(B, H_kv, T_q, max_kv_len, chunk_tokens, dtype)
+def decode_multi_split_tokens(B, H_q, H_kv, T_q, max_kv_len, chunk_tokens=0,
+                              dtype=DTYPE_BF16) -> int:
+    r = lib().gqa_attn_decode_multi_split_tokens(B, H_q, H_kv, T_q, max_kv_len, chunk_tokens,
+                                                 dtype)
     if r < 0:
         raise GQAError(-r, "gqa_attn_decode_multi_split_tokens")
     return r

@@ -46,13 +46,22 @@ int split_tokens(int B, int H_kv, int max_kv_len, int chunk_tokens, int dtype) {
   return (int)c;
 }
 
+// A multi-token decode whose G * T_q folded rows fit the decode kernel's
+// 16-row tile runs on the decode split kernel; larger folds run on the
+// multi-token kernel.
+bool multi_on_decode_kernel(int G, int T_q) { return (long long)G * T_q <= kMaxG; }
+
 // Effective keys per multi-token decode split, or a negative status.
-int multi_split_tokens(int B, int H_kv, int T_q, int max_kv_len, int chunk_tokens, int dtype) {
-  if (B < 1 || H_kv < 1 || T_q < 1 || max_kv_len < 1 || chunk_tokens < 0)
+int multi_split_tokens(int B, int H_q, int H_kv, int T_q, int max_kv_len, int chunk_tokens,
+                       int dtype) {
+  if (B < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || T_q < 1 || max_kv_len < 1 ||
+      chunk_tokens < 0)
     return -GQA_ERR_INVALID_ARG;
   if (T_q > max_kv_len) return -GQA_ERR_INVALID_ARG;
   if (dtype == GQA_DTYPE_F32) return -GQA_ERR_UNSUPPORTED;
   if (dtype != GQA_DTYPE_BF16) return -GQA_ERR_INVALID_ARG;
+  if (multi_on_decode_kernel(H_q / H_kv, T_q))
+    return split_tokens(B, H_kv, max_kv_len, chunk_tokens, dtype);
   if (chunk_tokens > 0) {
     if (chunk_tokens % kBf16ChunkQuantum != 0) return -GQA_ERR_INVALID_ARG;
     return chunk_tokens;
@@ -191,16 +200,16 @@ int gqa_attn_decode_combine(const void* q, const void* k_cache, const void* v_ca
                        gqa::kDecodeCombine);
 }
 
-int gqa_attn_decode_multi_split_tokens(int B, int H_kv, int T_q, int max_kv_len,
+int gqa_attn_decode_multi_split_tokens(int B, int H_q, int H_kv, int T_q, int max_kv_len,
                                        int chunk_tokens, int dtype) {
-  return multi_split_tokens(B, H_kv, T_q, max_kv_len, chunk_tokens, dtype);
+  return multi_split_tokens(B, H_q, H_kv, T_q, max_kv_len, chunk_tokens, dtype);
 }
 
 size_t gqa_attn_decode_multi_workspace_bytes(int B, int H_q, int H_kv, int d, int T_q,
                                              int max_kv_len, int chunk_tokens, int dtype) {
   if (H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || d != kD) return 0;
   if ((long long)(H_q / H_kv) * T_q > kMultiMaxRows) return 0;
-  const int chunk = multi_split_tokens(B, H_kv, T_q, max_kv_len, chunk_tokens, dtype);
+  const int chunk = multi_split_tokens(B, H_q, H_kv, T_q, max_kv_len, chunk_tokens, dtype);
   if (chunk <= 0) return 0;
   const int n_split = (max_kv_len + chunk - 1) / chunk;
   return ws_layout(B, H_q * T_q, n_split).total;
@@ -226,7 +235,7 @@ static int decode_multi_phases(const void* q, const void* k_cache, const void* v
   if ((long long)B * H_q * T_q > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
   if (d != kD || dtype != GQA_DTYPE_BF16 || (long long)(H_q / H_kv) * T_q > kMultiMaxRows)
     return GQA_ERR_UNSUPPORTED;
-  const int chunk = multi_split_tokens(B, H_kv, T_q, max_kv_len, chunk_tokens, dtype);
+  const int chunk = multi_split_tokens(B, H_q, H_kv, T_q, max_kv_len, chunk_tokens, dtype);
   if (chunk <= 0) return GQA_ERR_INVALID_ARG;
   const int n_split = (max_kv_len + chunk - 1) / chunk;
   const WsLayout wl = ws_layout(B, H_q * T_q, n_split);
@@ -251,9 +260,16 @@ static int decode_multi_phases(const void* q, const void* k_cache, const void* v
   p.max_kv_len = max_kv_len;
   p.chunk = chunk;
   p.n_split_max = n_split;
-  p.q_negate = scale < 0.f;
-  p.scale_log2 = fabsf(scale) * 1.4426950408889634f;
-  hipError_t e = gqa::launch_decode_multi(p, static_cast<hipStream_t>(stream), phases);
+  hipError_t e;
+  if (multi_on_decode_kernel(p.G, T_q)) {
+    p.q_negate = 0;
+    p.scale_log2 = scale * 1.4426950408889634f;   // the decode kernel takes the signed scale
+    e = gqa::launch_decode(p, true, static_cast<hipStream_t>(stream), phases);
+  } else {
+    p.q_negate = scale < 0.f;
+    p.scale_log2 = fabsf(scale) * 1.4426950408889634f;
+    e = gqa::launch_decode_multi(p, static_cast<hipStream_t>(stream), phases);
+  }
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 

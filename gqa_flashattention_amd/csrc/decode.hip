@@ -79,11 +79,13 @@ struct State {
   f32x4 o[8];    // O^T, d-tile dt: lane holds d = 8*(4*(lane/16)+i) + dt, query n
 };
 
-// `masked` (wave-uniform) is set for the wave's last block when it is
-// partial: keys at or past `kend` get weight 0.
+// `masked` (wave-uniform) is set for a block that holds keys some row may
+// not see: keys at or past `kend` (a partial last block), or past the
+// lane's row limit `vis_last` (the causal tail of a multi-token decode).
+// Such keys get weight 0.
 __device__ __forceinline__ void fold_block(State& st, const Block& blk, const bf16x8 (&qb)[4],
-                                           int key0, int kend, float scale_log2, int lane,
-                                           bool masked) {
+                                           int key0, int kend, int vis_last, float scale_log2,
+                                           int lane, bool masked) {
   const int g = lane >> 4;
   // S^T = K . Q^T for two 16-key sub-blocks.
   f32x4 s[2];
@@ -102,7 +104,8 @@ __device__ __forceinline__ void fold_block(State& st, const Block& blk, const bf
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (key0 + 16 * sb + 4 * g + i >= kend) s[sb][i] = kNegInf;
+        if (key0 + 16 * sb + 4 * g + i >= kend || key0 + 16 * sb + 4 * g + i > vis_last)
+          s[sb][i] = kNegInf;
   }
   float bmax = kNegInf;
 #pragma unroll
@@ -112,14 +115,17 @@ __device__ __forceinline__ void fold_block(State& st, const Block& blk, const bf
   bmax = wave_max_xor(bmax, 16);
   bmax = wave_max_xor(bmax, 32);
   const float m_new = fmaxf(st.m, bmax);
-  const float corr = fast_exp2(st.m - m_new);  // 0 on the first block (m = -inf)
+  // A row that has seen no visible key yet keeps m = -inf; its weights are
+  // taken against 0 (all exp2(-inf) = 0) so that no -inf - -inf appears.
+  const float mref = m_new == kNegInf ? 0.f : m_new;
+  const float corr = fast_exp2(st.m - mref);  // 0 on a row's first visible block (m = -inf)
   float psum = 0.f;
   float p[2][4];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[sb][i] = fast_exp2(s[sb][i] - m_new);
+      p[sb][i] = fast_exp2(s[sb][i] - mref);
       psum += p[sb][i];
     }
   st.l = st.l * corr + psum;
@@ -168,15 +174,20 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
   const __bf16* kbase = static_cast<const __bf16*>(p.k) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
   const __bf16* vbase = static_cast<const __bf16*>(p.v) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
 
-  // Q^T operand: query n = lane%16 of this KV head's group, zero past G.
+  // Q^T operand: row n = lane%16 of this KV head's M = G*T_q folded rows
+  // (row n is token n % T_q of head n / T_q; T_q = 1 for plain decode),
+  // zero past M.  Row n sees keys up to L - T_q + n % T_q.
   const int n = lane & 15;
   const int g = lane >> 4;
+  const int M = p.G * p.T_q;
+  const size_t row0 = ((size_t)b * p.H_q + (size_t)kvh * p.G) * p.T_q;
+  const bool row_ok = n < M;
+  const int vis_last = row_ok ? L - p.T_q + n % p.T_q : L - 1;
   bf16x8 qb[4];
   {
-    const bool ok = n < p.G;
-    const __bf16* qrow = q + ((size_t)b * p.H_q + (size_t)kvh * p.G + (ok ? n : 0)) * kD + 8 * g;
+    const __bf16* qrow = q + (row0 + (row_ok ? n : 0)) * kD + 8 * g;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) qb[kb] = as_bf16x8(ok ? ld16(qrow + 32 * kb) : u32x4{0, 0, 0, 0});
+    for (int kb = 0; kb < 4; ++kb) qb[kb] = as_bf16x8(row_ok ? ld16(qrow + 32 * kb) : u32x4{0, 0, 0, 0});
   }
 
   State st;
@@ -206,8 +217,12 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
     }
     Block A, B;
     auto load_i = [&](Block& bl, int i) { load_block(bl, rk, rv, off, i * kBlk * kD * 2); };
+    // Blocks that reach past L - T_q hold keys hidden from some rows.
+    const int first_hidden = L - p.T_q + 1;
     auto fold_i = [&](const Block& bl, int i) {
-      fold_block(st, bl, qb, ws + i * kBlk, we, p.scale_log2, lane, tail && i == nblk - 1);
+      const int key0 = ws + i * kBlk;
+      fold_block(st, bl, qb, key0, we, vis_last, p.scale_log2, lane,
+                 (tail && i == nblk - 1) || key0 + kBlk > first_hidden);
     };
     load_i(A, 0);
     for (int i = 0; i < nblk; i += 2) {
@@ -241,8 +256,8 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
   }
   __syncthreads();
 
-  const size_t part0 = ((size_t)b * p.H_q + (size_t)kvh * p.G) * p.n_split_max + split;
-  for (int e = threadIdx.x; e < p.G * kD; e += blockDim.x) {
+  const size_t part0 = row0 * p.n_split_max + split;
+  for (int e = threadIdx.x; e < M * kD; e += blockDim.x) {
     const int qn = e >> 7;
     const int dd = e & (kD - 1);
     float mw[kWaves];

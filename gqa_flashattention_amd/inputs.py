@@ -106,13 +106,17 @@ WORKLOADS = {
                                   H_kv=8, d=128, dtype="bf16", S_q=8192,
                                   S_kv=65536, causal=True, offset=57344),
     # Multi-token (speculative) decode on the 32K-key cache: 4 and 16 new
-    # tokens per sequence, G*T_q = 32 and 128 folded rows.
+    # tokens per sequence, G*T_q = 32 and 128 folded rows (and 2, below).
     "decode_multi_llama70b_32k_t4": Workload("decode_multi_llama70b_32k_t4", "decode_multi",
                                              B=1, H_q=64, H_kv=8, d=128, dtype="bf16",
                                              lens=(32768,), kv_cap=32768, T_q=4),
     "decode_multi_llama70b_32k_t16": Workload("decode_multi_llama70b_32k_t16", "decode_multi",
                                               B=1, H_q=64, H_kv=8, d=128, dtype="bf16",
                                               lens=(32768,), kv_cap=32768, T_q=16),
+    # T_q = 2 (one draft token): G*T_q = 16 rows, the decode kernel's tile.
+    "decode_multi_llama70b_32k_t2": Workload("decode_multi_llama70b_32k_t2", "decode_multi",
+                                             B=1, H_q=64, H_kv=8, d=128, dtype="bf16",
+                                             lens=(32768,), kv_cap=32768, T_q=2),
 }
 
 # Seed per workload: 20260000 + its position in the list above (1-based).

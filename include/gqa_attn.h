@@ -186,9 +186,12 @@ int gqa_attn_decode_combine(const void* q, const void* k_cache,
  *   max_kv_len, chunk_tokens, workspace: as for gqa_attn_decode, with the
  *            sizes from the two functions below.
  *
- * Two kernel launches on `stream`.  Each workgroup of the first stages one
- * split of one (sequence, KV head) through LDS and folds it into all G*T_q
- * rows; the second is the decode combine over the B*H_q*T_q rows.
+ * Two kernel launches on `stream`.  Each workgroup of the first folds one
+ * split of one (sequence, KV head) into all G*T_q rows -- for G*T_q <= 16
+ * with gqa_attn_decode's split kernel (the rows fill its 16-row tile),
+ * otherwise with a kernel that stages the split's K/V tiles in LDS for up
+ * to four 32-row groups; the second is the decode combine over the
+ * B*H_q*T_q rows.
  * Requirements: dtype == GQA_DTYPE_BF16, d == 128 and G*T_q <= 128 (else
  * GQA_ERR_UNSUPPORTED); 1 <= T_q <= max_kv_len <= kv_cap (else
  * GQA_ERR_INVALID_ARG).  T_q == 1 is plain decode (same results within
@@ -202,10 +205,11 @@ int gqa_attn_decode_multi(const void* q, const void* k_cache, const void* v_cach
 
 /*
  * Keys per multi-token decode split: `chunk_tokens` when positive (a
- * multiple of 128), else the library's automatic choice.  Returns a negative
- * gqa_status_t on invalid arguments (GQA_ERR_UNSUPPORTED for f32).
+ * multiple of 128), else the library's automatic choice (it depends on
+ * G * T_q, hence H_q).  Returns a negative gqa_status_t on invalid
+ * arguments (GQA_ERR_UNSUPPORTED for f32).
  */
-int gqa_attn_decode_multi_split_tokens(int B, int H_kv, int T_q, int max_kv_len,
+int gqa_attn_decode_multi_split_tokens(int B, int H_q, int H_kv, int T_q, int max_kv_len,
                                        int chunk_tokens, int dtype);
 
 /*

@@ -136,14 +136,18 @@ def test_prefill_rejects_before_launch(kw, status):
 
 def test_multi_split_and_workspace_rules():
     L = binding.lib()
-    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 4, 32768, 0, BF16) == 1024
-    assert L.gqa_attn_decode_multi_split_tokens(4, 8, 4, 131072, 0, BF16) == 2048
-    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 4, 100, 0, BF16) == 128    # tiny context
-    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 4, 32768, 384, BF16) == 384
-    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 4, 32768, 200, BF16) == -INVALID
-    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 4, 32768, 0, F32) == -UNSUPPORTED
-    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 0, 32768, 0, BF16) == -INVALID
-    assert L.gqa_attn_decode_multi_split_tokens(1, 8, 9, 8, 0, BF16) == -INVALID   # T_q > L
+    assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 4, 32768, 0, BF16) == 1024
+    assert L.gqa_attn_decode_multi_split_tokens(4, 64, 8, 4, 131072, 0, BF16) == 2048
+    assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 4, 100, 0, BF16) == 128    # tiny context
+    assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 4, 32768, 384, BF16) == 384
+    assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 4, 32768, 200, BF16) == -INVALID
+    assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 4, 32768, 0, F32) == -UNSUPPORTED
+    assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 0, 32768, 0, BF16) == -INVALID
+    assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 9, 8, 0, BF16) == -INVALID   # T_q > L
+    assert L.gqa_attn_decode_multi_split_tokens(1, 63, 8, 2, 32768, 0, BF16) == -INVALID
+    # G * T_q <= 16 runs on the decode split kernel and takes its split rule.
+    assert (L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 2, 32768, 0, BF16)
+            == L.gqa_attn_decode_split_tokens(1, 8, 32768, 0, BF16) == 512)
     n = L.gqa_attn_decode_multi_workspace_bytes(1, 64, 8, 128, 4, 32768, 1024, BF16)
     assert n >= 64 * 4 * 32 * (128 + 2) * 4
     assert L.gqa_attn_decode_multi_workspace_bytes(1, 64, 8, 128, 17, 32768, 0, BF16) == 0

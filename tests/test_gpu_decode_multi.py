@@ -39,7 +39,7 @@ def _workload(B, H_q, H_kv, T_q, lens, cap):
                            lens=lens, kv_cap=cap, T_q=T_q)
 
 
-@pytest.mark.parametrize("name", ["decode_multi_llama70b_32k_t4",
+@pytest.mark.parametrize("name", ["decode_multi_llama70b_32k_t2", "decode_multi_llama70b_32k_t4",
                                   "decode_multi_llama70b_32k_t16"])
 def test_decode_multi_workload(name):
     """The multi-token workloads at full size, automatic split (the bench's
@@ -69,7 +69,20 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("case", SMALL,
+SMALL_DECODE_KERNEL = [
+    # G * T_q <= 16: these run on the decode split kernel with a per-row tail.
+    (1, 8, 1, 2, (2,), 8, 0),                 # L = T_q
+    (1, 8, 1, 2, (3,), 8, 0),
+    (2, 8, 1, 2, (129, 257), 300, 128),       # last split holds one key: token 0 sees none of it
+    (1, 8, 1, 2, (641,), 700, 512),           # wave quarter 1 of the last split: one key
+    (2, 16, 4, 4, (33, 1000), 1024, 0),       # G = 4, T_q = 4
+    (1, 16, 8, 8, (4097,), 4100, 0),          # G = 2, T_q = 8
+    (1, 8, 8, 16, (300,), 300, 128),          # G = 1, T_q = 16
+    (1, 64, 8, 2, (5000,), 5000, 0),          # Llama geometry, T_q = 2
+]
+
+
+@pytest.mark.parametrize("case", SMALL + SMALL_DECODE_KERNEL,
                          ids=lambda c: f"B{c[0]}_Hq{c[1]}_Hkv{c[2]}_T{c[3]}_L{c[4]}_c{c[6]}")
 def test_decode_multi_shapes(case):
     """Row groups of 1, 2 and 4 (with padding rows), ragged tails, splits
@@ -77,14 +90,14 @@ def test_decode_multi_shapes(case):
     B, H_q, H_kv, T_q, lens, cap, chunk = case
     w = _workload(B, H_q, H_kv, T_q, lens, cap)
     banner("decode_multi_shapes", case)
-    x = inputs.make_decode_multi(w, device=DEV, seed=2000 + SMALL.index(case))
+    x = inputs.make_decode_multi(w, device=DEV, seed=2000 + (SMALL + SMALL_DECODE_KERNEL).index(case))
     o, lse = _run(x, w, chunk)
     ref_o, ref_lse = _oracle(x, w)
     _check(o, lse, ref_o, ref_lse, w, f"shapes {case}")
 
 
 def test_decode_multi_t1_matches_decode():
-    """T_q = 1 through the multi-token kernel against the oracle's plain
+    """T_q = 1 through gqa_attn_decode_multi against the oracle's plain
     decode, and within bf16 output rounding of gqa_attn_decode."""
     w = _workload(2, 64, 8, 1, (3000, 1234), 3000)
     banner("decode_multi_t1")
@@ -114,12 +127,13 @@ def test_decode_multi_scales(scale):
     _check(o, lse, ref_o, ref_lse, w, f"scale {scale}")
 
 
-@pytest.mark.parametrize("chunk", [0, 128])
-def test_decode_multi_max_jump(chunk):
+@pytest.mark.parametrize("chunk,T_q", [(0, 8), (128, 8), (0, 2), (128, 2)])
+def test_decode_multi_max_jump(chunk, T_q):
     """Keys of a later stretch scaled by 40 (and a few by 25, some inside the
-    causal tail): the per-row reference moves inside and between splits."""
-    w = _workload(2, 16, 2, 8, (5000, 3100), 5000)
-    banner("decode_multi_max_jump", chunk)
+    causal tail): the running max (T_q = 2, decode kernel) or the per-row
+    reference (T_q = 8, 64 rows) moves inside and between splits."""
+    w = _workload(2, 16, 2, T_q, (5000, 3100), 5000)
+    banner("decode_multi_max_jump", chunk, T_q)
     x = inputs.make_decode_multi(w, device=DEV, seed=23)
     x["k"][:, :, 3000:3100] *= 40.0
     x["k"][:, :, 4500:4510] *= 25.0
@@ -142,18 +156,20 @@ def test_decode_multi_split_invariance_and_determinism():
         assert torch.equal(o, o2) and torch.equal(lse, lse2), f"chunk {chunk} not deterministic"
 
 
-def test_decode_multi_tokens_are_causal():
+@pytest.mark.parametrize("T_q", [2, 4])
+def test_decode_multi_tokens_are_causal(T_q):
     """Changing the last cache row (the newest token's K/V) changes only the
-    newest token's outputs: earlier tokens never see it."""
-    w = _workload(1, 64, 8, 4, (1500,), 1500)
-    banner("decode_multi_causal_tail")
+    newest token's outputs: earlier tokens never see it (decode kernel at
+    T_q = 2, multi-token kernel at T_q = 4)."""
+    w = _workload(1, 64, 8, T_q, (1500,), 1500)
+    banner("decode_multi_causal_tail", T_q)
     x = inputs.make_decode_multi(w, device=DEV, seed=25)
     o1, _ = _run(x, w)
     x["k"][:, :, 1499] = torch.randn_like(x["k"][:, :, 1499]) * 3
     x["v"][:, :, 1499] = torch.randn_like(x["v"][:, :, 1499]) * 3
     o2, _ = _run(x, w)
-    assert torch.equal(o1[:, :, :3], o2[:, :, :3])
-    assert not torch.equal(o1[:, :, 3], o2[:, :, 3])
+    assert torch.equal(o1[:, :, :T_q - 1], o2[:, :, :T_q - 1])
+    assert not torch.equal(o1[:, :, T_q - 1], o2[:, :, T_q - 1])
 
 
 def test_decode_multi_phases_equal_one_call():
