@@ -28,6 +28,7 @@ from .attention import (  # noqa: F401
     kv_head_of,
     partial,
     merge,
+    merge_normalized,
     finalize,
     online_sweep,
 )

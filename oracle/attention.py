@@ -243,6 +243,32 @@ def merge(a, b):
     return m, l_a * sa + l_b * sb, o_a * sa[:, None] + o_b * sb[:, None]
 
 
+def merge_normalized(o_a, lse_a, o_b, lse_b):
+    """Stitch two attention results over disjoint key sets of the same query
+    rows, each given normalised with its LSE (chunk stitching).
+
+    A normalised result is the partial ``(m, l, O) = (lse, 1, O)``: its
+    weights relative to ``lse`` sum to one.  So the merge of ADR-0060@5a76ed4
+    §4 applies unchanged, followed by the one normalisation (``finalize``).
+    o_*: ``[..., d]``; lse_*: ``[...]`` natural log.  A side with
+    ``lse = -inf`` (no visible key) contributes nothing.
+    """
+    o_a = np.asarray(o_a, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    lse_a = np.asarray(lse_a, dtype=np.float64)
+    lse_b = np.asarray(lse_b, dtype=np.float64)
+    shape, d = lse_a.shape, o_a.shape[-1]
+    def as_partial(o, lse):
+        lse = lse.reshape(-1)
+        # An empty side gets weight 0 in the merge; its O (undefined) is zeroed
+        # so that 0 * NaN cannot reach the sum.
+        o = np.where(np.isneginf(lse)[:, None], 0.0, o.reshape(-1, d))
+        return lse, np.ones(lse.size), o
+
+    o, lse = finalize(merge(as_partial(o_a, lse_a), as_partial(o_b, lse_b)))
+    return o.reshape(*shape, d), lse.reshape(shape)
+
+
 def finalize(t):
     """Normalise once at the end: ``O / l`` and ``lse = m + ln(l)``
     (ADR-0060@5a76ed4 §4, "normalise once" after the merge)."""

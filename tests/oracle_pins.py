@@ -368,6 +368,49 @@ def pin_decode_multi_special_cases(O):
                what="L = T_q first token lse")
 
 
+
+# ------------------------------------------------------------ chunk stitching
+
+def pin_merge_normalized_chunks(O):
+    """Attention over keys split into two chunks at any cut, each chunk's
+    normalised (O, LSE) merged, equals attention over all keys (decode) and
+    the causal prefill of a chunk after a prefix; merging with an empty side
+    (lse = -inf) is the identity; the merge is symmetric."""
+    rng = _rng(28)
+    d, L = 8, 23
+    q = rng.standard_normal((5, d))
+    k = rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    ref_o, ref_l = O.attend_rows(q, k, v, 0.9, [L] * 5)
+    for cut in (1, 7, 22):
+        oa, la = O.attend_rows(q, k[:cut], v[:cut], 0.9, [cut] * 5)
+        ob, lb = O.attend_rows(q, k[cut:], v[cut:], 0.9, [L - cut] * 5)
+        o, lse = O.merge_normalized(oa, la, ob, lb)
+        _close(o, ref_o, what=f"stitch cut={cut}")
+        _close(lse, ref_l, what=f"stitch lse cut={cut}")
+        o2, l2 = O.merge_normalized(ob, lb, oa, la)
+        _close(o2, o, what="stitch symmetric")
+        _close(l2, lse, what="stitch symmetric lse")
+    empty = np.full(5, -np.inf)
+    o, lse = O.merge_normalized(ref_o, ref_l, np.full((5, d), np.nan), empty)
+    _close(o, ref_o, what="stitch with empty side")
+    _close(lse, ref_l, what="stitch with empty side lse")
+    # A causal chunk after a cached prefix: the prefix part is unmasked, the
+    # chunk's own part is causal; stitched, they are the causal prefill.
+    B, H_q, H_kv, S_q, off = 1, 4, 2, 6, 9
+    S_kv = off + S_q
+    qq = rng.standard_normal((B, H_q, S_q, d))
+    kk = rng.standard_normal((B, H_kv, S_kv, d))
+    vv = rng.standard_normal((B, H_kv, S_kv, d))
+    full_o, full_l = O.prefill(qq, kk, vv, S_kv, 0.5, causal=True, causal_offset=off)
+    pre_o, pre_l = O.prefill(qq, kk, vv, off, 0.5, causal=False)
+    new_o, new_l = O.prefill(qq, kk[:, :, off:], vv[:, :, off:], S_q, 0.5, causal=True,
+                             causal_offset=0)
+    o, lse = O.merge_normalized(pre_o, pre_l, new_o, new_l)
+    _close(o, full_o, what="prefix + chunk stitch")
+    _close(lse, full_l, what="prefix + chunk stitch lse")
+
+
 PINS = [
     pin_brute_force_decode,
     pin_brute_force_prefill,
@@ -386,4 +429,5 @@ PINS = [
     pin_brute_force_decode_multi,
     pin_decode_multi_sdpa,
     pin_decode_multi_special_cases,
+    pin_merge_normalized_chunks,
 ]

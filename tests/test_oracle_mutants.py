@@ -36,6 +36,10 @@ MUTANTS = {
                                "rows = q[b, heads].transpose(1, 0, 2).reshape(G * T_q, d)"),
     "multi_tokens_repeated": ("t = np.tile(np.arange(T_q, dtype=np.int64), G)",
                               "t = np.repeat(np.arange(T_q, dtype=np.int64), G)"),
+    "stitch_empty_o_kept": ("o = np.where(np.isneginf(lse)[:, None], 0.0, o.reshape(-1, d))",
+                            "o = o.reshape(-1, d)"),
+    "stitch_weights_swapped": ("o, lse = finalize(merge(as_partial(o_a, lse_a), as_partial(o_b, lse_b)))",
+                               "o, lse = finalize(merge(as_partial(o_a, lse_b), as_partial(o_b, lse_a)))"),
     "visible_ignored": ("vis = np.arange(j0, j1)[None, :] < vl[:, None]",
                         "vis = np.arange(j0, j1)[None, :] < L + 0 * vl[:, None]"),
 }
