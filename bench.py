@@ -44,8 +44,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--kv-copies", type=int, default=4)
-    ap.add_argument("--only", choices=["decode", "prefill", "both"], default="both",
-                    help="run one entry point only (for profiler runs)")
+    ap.add_argument("--only", choices=["decode", "prefill", "both", "merge"], default="both",
+                    help="run one entry point only (for profiler runs); 'merge' times "
+                         "gqa_attn_merge stitching two prefill_causal_8k-shaped outputs")
     ap.add_argument("--chunk", type=int, default=0, help="decode keys per split (0 = auto)")
     ap.add_argument("--decode-workload", default="decode_llama70b_32k",
                     help="decode workload name (the headline is decode_llama70b_32k; "
@@ -150,6 +151,46 @@ def cpu_baseline_prefill(w, x_cpu, seconds):
                       f"numpy fp64"}
 
 
+def bench_merge(args):
+    """gqa_attn_merge on two results of the prefill_causal_8k shape: rows =
+    64 heads x 8192 positions, O bf16 [rows, 128], LSE float32.  HBM bound:
+    reads 2 x (O + LSE), writes O + LSE."""
+    import torch
+    from gqa_flashattention_amd import binding as gq
+    rows, d = 64 * 8192, 128
+    g = torch.Generator(device="cuda:0").manual_seed(20260099)
+    mk = lambda: torch.randn(rows, d, device="cuda:0", generator=g).to(torch.bfloat16)
+    oa, ob = mk(), mk()
+    la = torch.randn(rows, device="cuda:0", generator=g) * 3
+    lb = torch.randn(rows, device="cuda:0", generator=g) * 3
+    out, lout = torch.empty_like(oa), torch.empty_like(la)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        gq.merge(oa, la, ob, lb, out=out, lse_out=lout, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        gq.merge(oa, la, ob, lb, out=out, lse_out=lout, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    nbytes = 3 * rows * d * 2 + 3 * rows * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    out_line = {
+        "metric": "decode KV GB/s (% HBM peak); causal prefill TFLOP/s (% bf16 MFMA peak)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "merge_prefill_8k (gqa_attn_merge)", "rows": rows, "d": d},
+        "roofline": {"bound": "hbm", "kernel": "merge_kernel<bf16>", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles("merge", "merge_prefill_8k"),
+                     "algorithmic_bytes_per_launch": nbytes, "launch_us_mean": round(us, 3)},
+    }
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -170,6 +211,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.only == "merge":
+        bench_merge(args)
+        return
 
     wd = inputs.WORKLOADS[args.decode_workload]
     dec_dtype = gq.DTYPE_F32 if wd.dtype == "f32" else gq.DTYPE_BF16

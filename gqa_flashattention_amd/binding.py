@@ -38,6 +38,7 @@ SIGNATURES = {
                                      _i, _i, _vp, _sz, _vp]),
     "gqa_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                               _f, _i, _vp]),
+    "gqa_attn_merge": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_longlong, _i, _i, _vp]),
     "gqa_attn_decode_multi_split_tokens": (_i, [_i, _i, _i, _i, _i, _i, _i]),
     "gqa_attn_decode_multi_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "gqa_attn_decode_multi": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
@@ -207,6 +208,29 @@ def decode_multi(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chun
                             workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, fn)
     return (out, lse) if return_lse else out
+
+
+def merge(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, return_lse=False, stream=None):
+    """``gqa_attn_merge`` on torch tensors: stitch two normalised results
+    (O ``[..., d]`` and LSE ``[...]`` float32) over disjoint key sets of the
+    same query rows.  ``out`` / ``lse_out`` may be the inputs themselves.
+    Returns ``o`` (and ``lse`` when ``return_lse``)."""
+    _require_gpu(o_a, lse_a, o_b, lse_b)
+    if o_a.shape != o_b.shape or lse_a.shape != lse_b.shape or lse_a.shape != o_a.shape[:-1]:
+        raise ValueError("o_a, o_b must be [..., d] and lse_a, lse_b their [...] LSEs")
+    if o_a.dtype != o_b.dtype or lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32:
+        raise TypeError("O inputs share one dtype; LSEs are float32")
+    d = o_a.shape[-1]
+    rows = lse_a.numel()
+    if out is None:
+        out = torch.empty_like(o_a)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    st = lib().gqa_attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out),
+                              _ptr(lse_out) if (return_lse or lse_out is not None) else None,
+                              rows, d, _dtype_code(o_a), _stream(stream))
+    _check(st, "gqa_attn_merge")
+    return (out, lse_out) if return_lse else out
 
 
 def prefill(q, k, v, S_kv=None, causal=True, causal_offset=0, scale=None, return_lse=False,

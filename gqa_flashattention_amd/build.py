@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqa_attn.so")
-SOURCES = ["api.hip", "decode.hip", "decode_multi.hip", "prefill.hip"]
+SOURCES = ["api.hip", "decode.hip", "decode_multi.hip", "merge.hip", "prefill.hip"]
 
 DEVICE_FLAGS = [
     "--offload-arch=gfx950",

@@ -303,6 +303,30 @@ int gqa_attn_decode_multi_combine(const void* q, const void* k_cache, const void
 
 #undef GQA_MULTI_ARGS
 
+int gqa_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                   void* o_out, float* lse_out, long long rows, int d, int dtype, void* stream) {
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out)) return GQA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(lse_a) & 3u) || (reinterpret_cast<uintptr_t>(lse_b) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse_out) & 3u))
+    return GQA_ERR_INVALID_ARG;
+  if (rows < 0 || d < 1) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16) return GQA_ERR_INVALID_ARG;
+  if (d != kD) return GQA_ERR_UNSUPPORTED;
+  if (rows > (1LL << 34)) return GQA_ERR_INVALID_ARG;
+  if (rows == 0) return GQA_OK;
+  gqa::MergeParams p;
+  p.o_a = o_a;
+  p.lse_a = lse_a;
+  p.o_b = o_b;
+  p.lse_b = lse_b;
+  p.o_out = o_out;
+  p.lse_out = lse_out;
+  p.rows = rows;
+  hipError_t e = gqa::launch_merge(p, dtype == GQA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
 int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int H_q, int H_kv, int d, int S_q, int S_kv, int kv_cap, int causal,
                      int causal_offset, float scale, int dtype, void* stream) {

@@ -39,6 +39,18 @@ struct PrefillParams {
   float scale_log2;     // |scale| * log2(e)
 };
 
+struct MergeParams {
+  const void* o_a;      // [rows, d]
+  const float* lse_a;   // [rows]
+  const void* o_b;      // [rows, d]
+  const float* lse_b;   // [rows]
+  void* o_out;          // [rows, d] (may alias o_a or o_b)
+  float* lse_out;       // [rows] or null (may alias lse_a or lse_b)
+  long long rows;
+};
+
+hipError_t launch_merge(const MergeParams& p, bool bf16, hipStream_t stream);
+
 // Decode launches: the split partial kernel, the combine kernel, or both.
 constexpr int kDecodePartial = 1;
 constexpr int kDecodeCombine = 2;

@@ -10,6 +10,7 @@
  *                     merged by a log-sum-exp combine.
  *   gqa_attn_prefill  a chunk of S_q query tokens, optionally causal with an
  *                     offset (the chunk follows causal_offset cached tokens).
+ *   gqa_attn_merge    stitches two (O, lse) results over disjoint key sets.
  *   gqa_attn_decode_multi
  *                     T_q >= 1 new tokens per sequence (speculative or
  *                     short-chunk decode) against the cache that holds them:
@@ -235,6 +236,29 @@ int gqa_attn_decode_multi_combine(const void* q, const void* k_cache, const void
                                   int H_q, int H_kv, int d, int T_q, int kv_cap,
                                   int max_kv_len, float scale, int dtype, int chunk_tokens,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stitching of two attention results for the same query rows over disjoint
+ * key sets (a prefix and a chunk, or two KV shards): the log-sum-exp merge
+ * of §4 applied to normalised results (each (O, lse) is the partial
+ * (m, l, O) = (lse, 1, O)).
+ *
+ *   o_a, o_b  [rows, d] dtype, with their LSEs lse_a, lse_b [rows] float32
+ *             (natural log, as this library exports them).  A row whose lse
+ *             is -inf (no visible key on that side) contributes nothing; its
+ *             O is not read into the sum (it may hold anything, NaN included).
+ *   o_out     [rows, d] dtype, written: (w_a O_a + w_b O_b) / (w_a + w_b)
+ *             with w = exp(lse - max(lse_a, lse_b)); rows empty on both
+ *             sides get O = 0.  May be the same buffer as o_a or o_b.
+ *   lse_out   [rows] float32, written when non-NULL: the merged LSE (-inf
+ *             for rows empty on both sides).  May be lse_a or lse_b.
+ *
+ * One kernel launch on `stream`; arithmetic in float32, output rounded to
+ * dtype (RNE).  Requirements: d == 128 (else GQA_ERR_UNSUPPORTED); rows >= 0
+ * (0 launches nothing).
+ */
+int gqa_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                   void* o_out, float* lse_out, long long rows, int d, int dtype, void* stream);
 
 /*
  * Prefill attention over a chunk of S_q queries (§5.4).

@@ -187,3 +187,25 @@ def _decode_multi(fn="gqa_attn_decode_multi", **kw):
                                 "gqa_attn_decode_multi_combine"])
 def test_decode_multi_rejects_before_launch(kw, status, fn):
     assert _decode_multi(fn, **kw) == status
+
+
+def _merge(**kw):
+    a = dict(oa=P, la=P, ob=P2, lb=P2, oo=P, lo=None, rows=100, d=128, dtype=BF16, stream=None)
+    a.update(kw)
+    return binding.lib().gqa_attn_merge(a["oa"], a["la"], a["ob"], a["lb"], a["oo"], a["lo"],
+                                        a["rows"], a["d"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(oa=None), INVALID),
+    (dict(lb=None), INVALID),
+    (dict(oo=None), INVALID),
+    (dict(ob=ctypes.c_void_p(0x200008)), INVALID),      # misaligned
+    (dict(lo=ctypes.c_void_p(0x200002)), INVALID),
+    (dict(rows=-1), INVALID),
+    (dict(dtype=3), INVALID),
+    (dict(d=64), UNSUPPORTED),
+    (dict(rows=0), OK),                                 # nothing to do, nothing launched
+])
+def test_merge_rejects_before_launch(kw, status):
+    assert _merge(**kw) == status
