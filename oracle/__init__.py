@@ -23,6 +23,8 @@ from .attention import (  # noqa: F401
     decode,
     decode_multi,
     decode_multi_visible_len,
+    decode_paged,
+    paged_gather,
     prefill,
     prefill_visible_len,
     kv_head_of,

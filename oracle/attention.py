@@ -155,6 +155,36 @@ def decode_multi(q, k_cache, v_cache, kv_lens, scale: float):
     return o, lse
 
 
+def paged_gather(pages, block_table, kv_lens, page_size: int):
+    """A paged cache laid out contiguously: sequence ``b``'s position ``j``
+    lives in physical page ``block_table[b, j // page_size]`` at row
+    ``j % page_size``.
+
+    pages: ``[num_pages, H_kv, page_size, d]``; block_table: ``[B, max_pages]``.
+    Returns ``[B, H_kv, max(kv_lens), d]`` float64 with positions past a
+    sequence's length set to NaN (they must never be read).
+    """
+    pages = np.asarray(pages, dtype=np.float64)
+    table = np.asarray(block_table, dtype=np.int64)
+    lens = np.asarray(kv_lens, dtype=np.int64).reshape(-1)
+    B, H_kv, d = table.shape[0], pages.shape[1], pages.shape[3]
+    top = int(lens.max())
+    out = np.full((B, H_kv, top, d), np.nan)
+    for b in range(B):
+        for j in range(int(lens[b])):
+            out[b, :, j] = pages[table[b, j // page_size], :, j % page_size]
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, kv_lens, page_size: int, scale: float):
+    """Decode of ``T_q >= 1`` new tokens per sequence (as ``decode_multi``)
+    over a paged K/V cache: the attention is unchanged, only the cache
+    layout differs (``paged_gather``).  q: ``[B, H_q, T_q, d]``."""
+    k = paged_gather(k_pages, block_table, kv_lens, page_size)
+    v = paged_gather(v_pages, block_table, kv_lens, page_size)
+    return decode_multi(q, k, v, kv_lens, scale)
+
+
 def prefill_visible_len(rows, S_kv: int, causal: bool, causal_offset: int):
     """Visible key count per query row of a prefill chunk.
 

@@ -411,6 +411,43 @@ def pin_merge_normalized_chunks(O):
     _close(lse, full_l, what="prefix + chunk stitch lse")
 
 
+
+# ------------------------------------------------------------- paged caches
+
+def pin_paged_gather_round_trip(O):
+    """Scatter contiguous caches into a shuffled page pool (written here with
+    explicit loops, pages shared by no one filled with NaN), gather back:
+    the valid positions come back unchanged and decode over the pages equals
+    decode over the original cache."""
+    rng = _rng(29)
+    for (B, H_q, H_kv, d, T_q, page, lens) in [(2, 4, 2, 4, 1, 4, (9, 16)),
+                                               (3, 8, 2, 4, 3, 2, (3, 7, 12)),
+                                               (1, 2, 1, 4, 2, 8, (5,))]:
+        top = max(lens)
+        k = rng.standard_normal((B, H_kv, top, d))
+        v = rng.standard_normal((B, H_kv, top, d))
+        q = rng.standard_normal((B, H_q, T_q, d))
+        max_pages = (top + page - 1) // page
+        num_pages = B * max_pages + 3
+        perm = rng.permutation(num_pages)
+        table = perm[:B * max_pages].reshape(B, max_pages)
+        kp = np.full((num_pages, H_kv, page, d), np.nan)
+        vp = np.full((num_pages, H_kv, page, d), np.nan)
+        for b in range(B):
+            for j in range(lens[b]):
+                for h in range(H_kv):
+                    kp[table[b, j // page], h, j % page] = k[b, h, j]
+                    vp[table[b, j // page], h, j % page] = v[b, h, j]
+        kg = O.paged_gather(kp, table, np.array(lens), page)
+        for b in range(B):
+            assert np.array_equal(kg[b, :, :lens[b]], k[b, :, :lens[b]]), "gather lost a row"
+            assert np.all(np.isnan(kg[b, :, lens[b]:])), "gather read past a length"
+        o, lse = O.decode_paged(q, kp, vp, table, np.array(lens), page, 0.6)
+        ro, rl = O.decode_multi(q, k, v, np.array(lens), 0.6)
+        _close(o, ro, what="paged decode")
+        _close(lse, rl, what="paged decode lse")
+
+
 PINS = [
     pin_brute_force_decode,
     pin_brute_force_prefill,
@@ -430,4 +467,5 @@ PINS = [
     pin_decode_multi_sdpa,
     pin_decode_multi_special_cases,
     pin_merge_normalized_chunks,
+    pin_paged_gather_round_trip,
 ]

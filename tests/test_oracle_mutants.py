@@ -40,6 +40,10 @@ MUTANTS = {
                             "o = o.reshape(-1, d)"),
     "stitch_weights_swapped": ("o, lse = finalize(merge(as_partial(o_a, lse_a), as_partial(o_b, lse_b)))",
                                "o, lse = finalize(merge(as_partial(o_a, lse_b), as_partial(o_b, lse_a)))"),
+    "paged_row_shift": ("out[b, :, j] = pages[table[b, j // page_size], :, j % page_size]",
+                        "out[b, :, j] = pages[table[b, j // page_size], :, (j + 1) % page_size]"),
+    "paged_wrong_page": ("out[b, :, j] = pages[table[b, j // page_size], :, j % page_size]",
+                         "out[b, :, j] = pages[table[b, j % page_size], :, j % page_size]"),
     "visible_ignored": ("vis = np.arange(j0, j1)[None, :] < vl[:, None]",
                         "vis = np.arange(j0, j1)[None, :] < L + 0 * vl[:, None]"),
 }
