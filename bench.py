@@ -110,12 +110,17 @@ def cpu_baseline_decode(w, x_cpu, seconds):
     """Oracle over whole decode calls of the workload, repeated to ~seconds."""
     import numpy as np
     import oracle
-    q, k, v = (x_cpu[n] for n in ("q", "k", "v"))
     lens = np.array(w.lens)
-    fn = oracle.decode_multi if w.kind == "decode_multi" else oracle.decode
+    if w.kind == "decode_paged":
+        args = (x_cpu["q"], x_cpu["k_pages"], x_cpu["v_pages"], x_cpu["block_table"], lens,
+                w.page_size, w.scale)
+        fn = oracle.decode_paged
+    else:
+        args = (x_cpu["q"], x_cpu["k"], x_cpu["v"], lens, w.scale)
+        fn = oracle.decode_multi if w.kind == "decode_multi" else oracle.decode
     reps, t0 = 0, time.perf_counter()
     while True:
-        fn(q, k, v, lens, w.scale)
+        fn(*args)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1000:
@@ -217,17 +222,30 @@ def main():
 
     wd = inputs.WORKLOADS[args.decode_workload]
     dec_dtype = gq.DTYPE_F32 if wd.dtype == "f32" else gq.DTYPE_BF16
-    multi = wd.kind == "decode_multi"
+    multi = wd.kind in ("decode_multi", "decode_paged")
+    paged = wd.kind == "decode_paged"
     wp = inputs.WORKLOADS[args.prefill_workload]
     do_dec = args.only in ("decode", "both")
     do_pre = args.only in ("prefill", "both")
 
     # ---- inputs, resident in HBM before timing
     if do_dec:
-        make = inputs.make_decode_multi if multi else inputs.make_decode
+        if paged:
+            make = lambda w, device, seed: inputs.make_decode_paged(w, w.page_size, device=device,
+                                                                    seed=seed)
+        else:
+            make = inputs.make_decode_multi if multi else inputs.make_decode
         copies = [make(wd, device=dev, seed=inputs.SEEDS[wd.name] + 100 * i)
                   for i in range(max(1, args.kv_copies))]
-        if multi:
+        if paged:
+            need = gq.decode_paged_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.T_q,
+                                                   wd.page_size, wd.max_kv_len, args.chunk,
+                                                   dec_dtype)
+            chunk = gq.decode_paged_split_tokens(wd.B, wd.H_q, wd.H_kv, wd.T_q, wd.page_size,
+                                                 wd.max_kv_len, args.chunk, dec_dtype)
+            for x in copies:          # only the pages are read; drop the contiguous copy
+                del x["k"], x["v"]
+        elif multi:
             need = gq.decode_multi_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.T_q,
                                                    wd.max_kv_len, args.chunk, dec_dtype)
             chunk = gq.decode_multi_split_tokens(wd.B, wd.H_q, wd.H_kv, wd.T_q, wd.max_kv_len,
@@ -249,6 +267,11 @@ def main():
 
     def decode_call(i, phase="both"):
         x = copies[i % len(copies)]
+        if paged:
+            gq.decode_paged(x["q"], x["k_pages"], x["v_pages"], x["block_table"], x["kv_lens"],
+                            max_kv_len=wd.max_kv_len, scale=wd.scale, chunk_tokens=args.chunk,
+                            out=o_dec, workspace=ws, stream=stream, phase=phase)
+            return
         fn = gq.decode_multi if multi else gq.decode
         fn(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=wd.max_kv_len,
            scale=wd.scale, chunk_tokens=args.chunk, out=o_dec, workspace=ws,
@@ -318,8 +341,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": " + ".join(n for n, on in ((wd.name, do_dec), (wp.name, do_pre)) if on),
                    "decode": {"B": wd.B, "H_q": wd.H_q, "H_kv": wd.H_kv, "d": wd.d,
-                              "T_q": wd.T_q, "entry_point": "gqa_attn_decode_multi" if multi
-                              else "gqa_attn_decode",
+                              "T_q": wd.T_q, "page_size": wd.page_size or None,
+                              "entry_point": "gqa_attn_decode_paged" if paged else
+                              "gqa_attn_decode_multi" if multi else "gqa_attn_decode",
                               "kv_lens": list(wd.lens), "kv_copies": len(copies) if do_dec else 0,
                               "keys_per_split": chunk if do_dec else None},
                    "prefill": {"B": wp.B, "H_q": wp.H_q, "H_kv": wp.H_kv, "d": wp.d,
@@ -376,7 +400,9 @@ def main():
     if not args.no_cpu_baseline:
         import numpy as np  # noqa: F401
         if do_dec:
-            xc = {n: copies[0][n].float().cpu().numpy() for n in ("q", "k", "v")}
+            names = ("q", "k_pages", "v_pages", "block_table") if paged else ("q", "k", "v")
+            xc = {n: (copies[0][n].cpu().numpy() if n == "block_table"
+                      else copies[0][n].float().cpu().numpy()) for n in names}
             out["cpu_baseline"] = cpu_baseline_decode(wd, xc, args.cpu_seconds)
             del xc
         if do_pre:

@@ -39,6 +39,14 @@ SIGNATURES = {
     "gqa_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                               _f, _i, _vp]),
     "gqa_attn_merge": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_longlong, _i, _i, _vp]),
+    "gqa_attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                   _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "gqa_attn_decode_paged_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                           _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "gqa_attn_decode_paged_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                           _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "gqa_attn_decode_paged_split_tokens": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "gqa_attn_decode_paged_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "gqa_attn_decode_multi_split_tokens": (_i, [_i, _i, _i, _i, _i, _i, _i]),
     "gqa_attn_decode_multi_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "gqa_attn_decode_multi": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
@@ -206,6 +214,60 @@ def decode_multi(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chun
                             _ptr(lse) if return_lse else None, B, H_q, H_kv, d, T_q, kv_cap,
                             max_kv_len, scale, dt, chunk_tokens, _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, fn)
+    return (out, lse) if return_lse else out
+
+
+def decode_paged_split_tokens(B, H_q, H_kv, T_q, page_size, max_kv_len, chunk_tokens=0,
+                              dtype=DTYPE_BF16) -> int:
+    r = lib().gqa_attn_decode_paged_split_tokens(B, H_q, H_kv, T_q, page_size, max_kv_len,
+                                                 chunk_tokens, dtype)
+    if r < 0:
+        raise GQAError(-r, "gqa_attn_decode_paged_split_tokens")
+    return r
+
+
+def decode_paged_workspace_bytes(B, H_q, H_kv, d, T_q, page_size, max_kv_len, chunk_tokens=0,
+                                 dtype=DTYPE_BF16) -> int:
+    n = lib().gqa_attn_decode_paged_workspace_bytes(B, H_q, H_kv, d, T_q, page_size, max_kv_len,
+                                                    chunk_tokens, dtype)
+    if n == 0:
+        raise GQAError(1, "gqa_attn_decode_paged_workspace_bytes")
+    return n
+
+
+def decode_paged(q, k_pages, v_pages, block_table, kv_lens, max_kv_len, scale=None,
+                 chunk_tokens=0, return_lse=False, out=None, lse=None, workspace=None,
+                 stream=None, phase="both"):
+    """``gqa_attn_decode_paged`` on torch tensors.
+
+    q ``[B,H_q,T_q,d]`` bf16; k_pages/v_pages ``[num_pages,H_kv,page_size,d]``
+    bf16; block_table ``[B,max_pages]`` and kv_lens ``[B]`` int32 on the
+    device.  Returns ``o`` (and ``lse`` ``[B,H_q,T_q]`` when ``return_lse``).
+    """
+    _require_gpu(q, k_pages, v_pages, block_table, kv_lens)
+    B, H_q, T_q, d = q.shape
+    num_pages, H_kv, page_size, _ = k_pages.shape
+    if block_table.dtype != torch.int32 or kv_lens.dtype != torch.int32:
+        raise TypeError("block_table and kv_lens must be int32")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q, T_q), dtype=torch.float32, device=q.device)
+    need = decode_paged_workspace_bytes(B, H_q, H_kv, d, T_q, page_size, max_kv_len,
+                                        chunk_tokens, dt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    fn = {"both": "gqa_attn_decode_paged", "partial": "gqa_attn_decode_paged_partial",
+          "combine": "gqa_attn_decode_paged_combine"}[phase]
+    st = getattr(lib(), fn)(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                            _ptr(kv_lens), _ptr(out), _ptr(lse) if return_lse else None,
+                            B, H_q, H_kv, d, T_q, page_size, block_table.shape[1],
+                            num_pages, int(max_kv_len), scale, dt, chunk_tokens,
+                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream(stream))
     _check(st, fn)
     return (out, lse) if return_lse else out
 

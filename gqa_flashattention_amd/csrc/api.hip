@@ -79,6 +79,34 @@ int multi_split_tokens(int B, int H_q, int H_kv, int T_q, int max_kv_len, int ch
   return (int)c;
 }
 
+// log2 of a paged-cache page size, or -1 unless it is a power of two in
+// [16, 65536].
+int page_shift_of(int page_size) {
+  if (page_size < 16 || page_size > 65536 || (page_size & (page_size - 1))) return -1;
+  int sh = 0;
+  while ((1 << sh) < page_size) ++sh;
+  return sh;
+}
+
+// Keys per split of a paged-cache decode, or a negative status: the rule of
+// the kernel the fold runs on, with splits small enough that the decode
+// kernel's wave ranges span at most 64 pages and the multi-token kernel's
+// splits at most 128 (each keeps its page numbers in one or two registers).
+int paged_split_tokens(int B, int H_q, int H_kv, int T_q, int page_size, int max_kv_len,
+                       int chunk_tokens, int dtype) {
+  const int sh = page_shift_of(page_size);
+  if (sh < 0) return -GQA_ERR_INVALID_ARG;
+  int c = multi_split_tokens(B, H_q, H_kv, T_q, max_kv_len, chunk_tokens, dtype);
+  if (c <= 0) return c;
+  const bool dk = multi_on_decode_kernel(H_q / H_kv, T_q);
+  const long long limit = dk ? 4LL * 63 * page_size : 127LL * page_size;   // keys per split
+  if (c > limit) {
+    if (chunk_tokens > 0) return -GQA_ERR_INVALID_ARG;
+    c = (int)(limit / kBf16ChunkQuantum * kBf16ChunkQuantum);
+  }
+  return c;
+}
+
 // Workspace: [partial O] [partial (m, l)], each region 256-byte aligned.
 struct WsLayout {
   size_t ml_off, total;
@@ -161,6 +189,10 @@ static int decode_phases(const void* q, const void* k_cache, const void* v_cache
   p.G = H_q / H_kv;
   p.kv_cap = kv_cap;
   p.T_q = 1;
+  p.block_table = nullptr;
+  p.max_pages = 0;
+  p.page_shift = 0;
+  p.num_pages = 0;
   p.max_kv_len = max_kv_len;
   p.chunk = chunk;
   p.n_split_max = n_split;
@@ -257,6 +289,10 @@ static int decode_multi_phases(const void* q, const void* k_cache, const void* v
   p.G = H_q / H_kv;
   p.kv_cap = kv_cap;
   p.T_q = T_q;
+  p.block_table = nullptr;
+  p.max_pages = 0;
+  p.page_shift = 0;
+  p.num_pages = 0;
   p.max_kv_len = max_kv_len;
   p.chunk = chunk;
   p.n_split_max = n_split;
@@ -302,6 +338,114 @@ int gqa_attn_decode_multi_combine(const void* q, const void* k_cache, const void
 }
 
 #undef GQA_MULTI_ARGS
+
+int gqa_attn_decode_paged_split_tokens(int B, int H_q, int H_kv, int T_q, int page_size,
+                                       int max_kv_len, int chunk_tokens, int dtype) {
+  return paged_split_tokens(B, H_q, H_kv, T_q, page_size, max_kv_len, chunk_tokens, dtype);
+}
+
+size_t gqa_attn_decode_paged_workspace_bytes(int B, int H_q, int H_kv, int d, int T_q,
+                                             int page_size, int max_kv_len, int chunk_tokens,
+                                             int dtype) {
+  if (H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || d != kD) return 0;
+  if ((long long)(H_q / H_kv) * T_q > kMultiMaxRows) return 0;
+  const int chunk = paged_split_tokens(B, H_q, H_kv, T_q, page_size, max_kv_len, chunk_tokens, dtype);
+  if (chunk <= 0) return 0;
+  const int n_split = (max_kv_len + chunk - 1) / chunk;
+  return ws_layout(B, H_q * T_q, n_split).total;
+}
+
+static int decode_paged_phases(const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int32_t* kv_lens, void* o,
+                               float* lse, int B, int H_q, int H_kv, int d, int T_q,
+                               int page_size, int max_pages_per_seq, int num_pages,
+                               int max_kv_len, float scale, int dtype, int chunk_tokens,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               int phases) {
+  if (!q || !k_pages || !v_pages || !block_table || !kv_lens || !o) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
+    return GQA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(kv_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return GQA_ERR_INVALID_ARG;
+  if (B < 1 || H_q < 1 || H_kv < 1 || d < 1 || T_q < 1 || max_kv_len < 1 || num_pages < 1 ||
+      max_pages_per_seq < 1)
+    return GQA_ERR_INVALID_ARG;
+  if (H_q % H_kv != 0 || T_q > max_kv_len) return GQA_ERR_INVALID_ARG;
+  const int sh = page_shift_of(page_size);
+  if (sh < 0) return GQA_ERR_INVALID_ARG;
+  if ((long long)max_pages_per_seq * page_size < max_kv_len) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16) return GQA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (chunk_tokens < 0) return GQA_ERR_INVALID_ARG;
+  if (B > 65535 || H_kv > 65535) return GQA_ERR_INVALID_ARG;
+  if ((long long)B * H_q * T_q > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
+  if (d != kD || dtype != GQA_DTYPE_BF16 || (long long)(H_q / H_kv) * T_q > kMultiMaxRows)
+    return GQA_ERR_UNSUPPORTED;
+  const int chunk = paged_split_tokens(B, H_q, H_kv, T_q, page_size, max_kv_len, chunk_tokens, dtype);
+  if (chunk <= 0) return GQA_ERR_INVALID_ARG;
+  const int n_split = (max_kv_len + chunk - 1) / chunk;
+  const WsLayout wl = ws_layout(B, H_q * T_q, n_split);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u)) return GQA_ERR_WORKSPACE;
+  if (workspace_bytes < wl.total) return GQA_ERR_WORKSPACE;
+
+  gqa::DecodeParams p;
+  p.q = q;
+  p.k = k_pages;
+  p.v = v_pages;
+  p.kv_lens = kv_lens;
+  p.o = o;
+  p.lse = lse;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+  p.B = B;
+  p.H_q = H_q;
+  p.H_kv = H_kv;
+  p.G = H_q / H_kv;
+  p.kv_cap = 0;
+  p.T_q = T_q;
+  p.block_table = block_table;
+  p.max_pages = max_pages_per_seq;
+  p.page_shift = sh;
+  p.num_pages = num_pages;
+  p.max_kv_len = max_kv_len;
+  p.chunk = chunk;
+  p.n_split_max = n_split;
+  hipError_t e;
+  if (multi_on_decode_kernel(p.G, T_q)) {
+    p.q_negate = 0;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    e = gqa::launch_decode(p, true, static_cast<hipStream_t>(stream), phases);
+  } else {
+    p.q_negate = scale < 0.f;
+    p.scale_log2 = fabsf(scale) * 1.4426950408889634f;
+    e = gqa::launch_decode_multi(p, static_cast<hipStream_t>(stream), phases);
+  }
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+#define GQA_PAGED_ARGS                                                                       \
+  q, k_pages, v_pages, block_table, kv_lens, o, lse, B, H_q, H_kv, d, T_q, page_size,          \
+      max_pages_per_seq, num_pages, max_kv_len, scale, dtype, chunk_tokens, workspace,           \
+      workspace_bytes, stream
+#define GQA_PAGED_PARAMS                                                                     \
+  const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,         \
+      const int32_t *kv_lens, void *o, float *lse, int B, int H_q, int H_kv, int d, int T_q,      \
+      int page_size, int max_pages_per_seq, int num_pages, int max_kv_len, float scale,         \
+      int dtype, int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream
+
+int gqa_attn_decode_paged(GQA_PAGED_PARAMS) {
+  return decode_paged_phases(GQA_PAGED_ARGS, gqa::kDecodePartial | gqa::kDecodeCombine);
+}
+int gqa_attn_decode_paged_partial(GQA_PAGED_PARAMS) {
+  return decode_paged_phases(GQA_PAGED_ARGS, gqa::kDecodePartial);
+}
+int gqa_attn_decode_paged_combine(GQA_PAGED_PARAMS) {
+  return decode_paged_phases(GQA_PAGED_ARGS, gqa::kDecodeCombine);
+}
+
+#undef GQA_PAGED_ARGS
+#undef GQA_PAGED_PARAMS
 
 int gqa_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                    void* o_out, float* lse_out, long long rows, int d, int dtype, void* stream) {

@@ -72,6 +72,24 @@ __device__ __forceinline__ void load_block(Block& blk, __amdgpu_buffer_rsrc_t rk
     blk.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, off.v[j >> 2] + (j & 3) * kD * 2, soff, 2);
 }
 
+// Paged cache: the two 16-key sub-blocks of a block each lie in one page
+// (page sizes are powers of two >= 16 and blocks start at multiples of 32),
+// so each gets its own resources: base = the sub-block's first row in its
+// page, size = the sub-block's rows below the wave's last key (0 when the
+// sub-block starts past it: all loads then read zeros).
+__device__ __forceinline__ void load_block_paged(Block& blk, const __amdgpu_buffer_rsrc_t (&rk)[2],
+                                                 const __amdgpu_buffer_rsrc_t (&rv)[2],
+                                                 const BlockOffsets& off) {
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      blk.k[sb][kb] = __builtin_amdgcn_raw_buffer_load_b128(rk[sb], off.k[0] + 64 * kb, 0, 2);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    blk.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv[j >> 2], off.v[0] + (j & 3) * kD * 2, 0, 2);
+}
+
 // Running state of one wave: query n = lane % 16 (rows >= G are padding).
 struct State {
   float m;       // running max of log2-domain scores (same on the 4 lanes of n)
@@ -155,7 +173,9 @@ __device__ __forceinline__ void fold_block(State& st, const Block& blk, const bf
 
 }  // namespace
 
-// Grid: (n_split_max, H_kv, B); block: 256 threads.
+// Grid: (n_split_max, H_kv, B); block: 256 threads.  kPaged: K/V live in a
+// page pool addressed through the block table (DecodeParams::block_table).
+template <bool kPaged>
 __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParams p) {
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -171,8 +191,9 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
   const int we = min(ws + quarter, end);
 
   const __bf16* q = static_cast<const __bf16*>(p.q);
-  const __bf16* kbase = static_cast<const __bf16*>(p.k) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
-  const __bf16* vbase = static_cast<const __bf16*>(p.v) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
+  // Contiguous cache: this (sequence, KV head)'s rows (unused when paged).
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + (kPaged ? 0 : ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD);
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + (kPaged ? 0 : ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD);
 
   // Q^T operand: row n = lane%16 of this KV head's M = G*T_q folded rows
   // (row n is token n % T_q of head n / T_q; T_q = 1 for plain decode),
@@ -202,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
     // last block of the wave's range can be partial (masked).
     const int nblk = (we - ws + kBlk - 1) / kBlk;
     const bool tail = (we - ws) % kBlk != 0;
-    const unsigned bytes = (unsigned)(we - ws) * (kD * 2);
+    const unsigned bytes = kPaged ? 0u : (unsigned)(we - ws) * (kD * 2);
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (size_t)ws * kD), (short)0, bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv =
@@ -215,8 +236,40 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
       off.v[0] = 4 * g * (kD * 2) + 16 * r;
       off.v[1] = off.v[0] + 16 * (kD * 2);
     }
+    // Paged: lane j holds the physical page of the wave's logical page
+    // lp0 + j (at most 64 pages per wave range, checked on the host).
+    const int shift = p.page_shift;
+    const int lp0 = ws >> shift;
+    int pt = 0;
+    if constexpr (kPaged) {
+      const int npg = ((we - 1) >> shift) - lp0 + 1;
+      if (lane < npg) pt = min(max(p.block_table[(size_t)b * p.max_pages + lp0 + lane], 0), p.num_pages - 1);
+    }
     Block A, B;
-    auto load_i = [&](Block& bl, int i) { load_block(bl, rk, rv, off, i * kBlk * kD * 2); };
+    auto load_i = [&](Block& bl, int i) {
+      if constexpr (kPaged) {
+        const size_t page_elems = (size_t)p.H_kv * (kD << shift);
+        const size_t head_elems = (size_t)kvh * (kD << shift);
+        __amdgpu_buffer_rsrc_t rks[2], rvs[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int pos = ws + i * kBlk + 16 * sb;
+          // readfirstlane: the page is wave-uniform, and saying so keeps the
+          // resources in scalar registers (no per-lane loop around the loads).
+          const int pp = __builtin_amdgcn_readfirstlane(
+              __builtin_amdgcn_readlane(pt, min((pos >> shift) - lp0, 63)));
+          const size_t e = (size_t)pp * page_elems + head_elems + (size_t)(pos & ((1 << shift) - 1)) * kD;
+          const unsigned nb = __builtin_amdgcn_readfirstlane((unsigned)max(0, min(16, we - pos)) * (kD * 2));
+          rks[sb] = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(static_cast<const __bf16*>(p.k) + e), (short)0, nb, 0x00020000);
+          rvs[sb] = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(static_cast<const __bf16*>(p.v) + e), (short)0, nb, 0x00020000);
+        }
+        load_block_paged(bl, rks, rvs, off);
+      } else {
+        load_block(bl, rk, rv, off, i * kBlk * kD * 2);
+      }
+    };
     // Blocks that reach past L - T_q hold keys hidden from some rows.
     const int first_hidden = L - p.T_q + 1;
     auto fold_i = [&](const Block& bl, int i) {
@@ -520,7 +573,10 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, i
   if (phases & kDecodePartial) {
     dim3 grid(p.n_split_max, p.H_kv, p.B);
     if (bf16) {
-      hipLaunchKernelGGL(decode_partial_bf16_kernel, grid, dim3(256), 0, stream, p);
+      if (p.block_table != nullptr)
+        hipLaunchKernelGGL(decode_partial_bf16_kernel<true>, grid, dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL(decode_partial_bf16_kernel<false>, grid, dim3(256), 0, stream, p);
     } else {
       hipLaunchKernelGGL(decode_partial_f32_kernel, grid, dim3(256), 0, stream, p);
     }

@@ -119,8 +119,9 @@ constexpr int kRedFloats = 32 * kRedStride;
 
 }  // namespace
 
-// Grid: (n_split_max, H_kv, B); block: 64 * W threads.
-template <int R>
+// Grid: (n_split_max, H_kv, B); block: 64 * W threads.  kPaged: K/V live in
+// a page pool addressed through the block table.
+template <int R, bool kPaged>
 __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_partial_kernel(
     DecodeParams p) {
   using S = typename MqLaunch<R>::S;
@@ -155,8 +156,8 @@ __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_part
   const int vis_last = row_ok ? min(L - p.T_q + row % p.T_q, end - 1) : end - 1;
 
   const size_t row0 = ((size_t)b * p.H_q + (size_t)kvh * p.G) * p.T_q;   // first folded row
-  const __bf16* Kg = static_cast<const __bf16*>(p.k) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
-  const __bf16* Vg = static_cast<const __bf16*>(p.v) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
+  const __bf16* Kg = static_cast<const __bf16*>(p.k) + (kPaged ? 0 : ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD);
+  const __bf16* Vg = static_cast<const __bf16*>(p.v) + (kPaged ? 0 : ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD);
 
   // Q^T operand (B of S^T): row `row`, d = 16*kk + 8*h2 .. +8.  A negative
   // scale is applied exactly by flipping Q's sign bits.
@@ -208,18 +209,54 @@ __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_part
     ld_off[0][i] = r * kRowBytes + 16 * k_swz(r, lane & 15);   // XOR is an involution
     ld_off[1][i] = r * kRowBytes + 16 * v_swz(r, lane & 15);
   }
+  // Paged: lane j of pt[0] / pt[1] holds the physical page of the split's
+  // logical page lp0 + j / lp0 + 64 + j (at most 128 pages per split,
+  // checked on the host); entries are clamped into the pool.
+  const int shift = p.page_shift;
+  const int lp0 = start >> shift;
+  int pt[2] = {0, 0};
+  if constexpr (kPaged) {
+    const int npg = ((end - 1) >> shift) - lp0 + 1;
+    const int32_t* trow = p.block_table + (size_t)b * p.max_pages + lp0;
+    if (lane < npg) pt[0] = min(max(trow[lane], 0), p.num_pages - 1);
+    if (lane + 64 < npg) pt[1] = min(max(trow[lane + 64], 0), p.num_pages - 1);
+  }
   auto load_step = [&](auto slot_c, int s) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
     const int key0 = start + s * S::kStep;
-    const unsigned bytes = (unsigned)(end - key0) * kRowBytes;
-    const u32x4 rk = buffer_rsrc(Kg + (size_t)key0 * kD, bytes);
-    const u32x4 rv = buffer_rsrc(Vg + (size_t)key0 * kD, bytes);
+    if constexpr (kPaged) {
+      // One resource per 1 KiB instruction (4 rows, always inside one page):
+      // based so that the instruction's lane offsets land on its rows, and
+      // ending at the split's last key (rows past it read as zeros).
+      const size_t page_elems = (size_t)p.H_kv * (kD << shift);
+      const size_t head_elems = (size_t)kvh * (kD << shift);
 #pragma unroll
-    for (int i = 0; i < S::kInsts; ++i)
-      dma_load_x4(ld_off[0][i], rk, lds_k0 + slot * S::kStepBytes + 4 * (S::kInsts * wave + i) * kRowBytes);
+      for (int i = 0; i < S::kInsts; ++i) {
+        const int r0 = 4 * (S::kInsts * wave + i);
+        const int pos = key0 + r0;
+        const int idx = min((pos >> shift) - lp0, 127);
+        const int pp = idx < 64 ? __builtin_amdgcn_readlane(pt[0], idx)
+                                : __builtin_amdgcn_readlane(pt[1], idx - 64);
+        const size_t e = (size_t)pp * page_elems + head_elems + (size_t)(pos & ((1 << shift) - 1)) * kD;
+        const unsigned nb = (unsigned)(r0 + max(0, min(4, end - pos))) * kRowBytes;
+        const uintptr_t kb = reinterpret_cast<uintptr_t>(static_cast<const __bf16*>(p.k) + e) - (uintptr_t)r0 * kRowBytes;
+        const uintptr_t vb = reinterpret_cast<uintptr_t>(static_cast<const __bf16*>(p.v) + e) - (uintptr_t)r0 * kRowBytes;
+        dma_load_x4(ld_off[0][i], buffer_rsrc(reinterpret_cast<const void*>(kb), nb),
+                    lds_k0 + slot * S::kStepBytes + 4 * (S::kInsts * wave + i) * kRowBytes);
+        dma_load_x4(ld_off[1][i], buffer_rsrc(reinterpret_cast<const void*>(vb), nb),
+                    lds_v0 + slot * S::kStepBytes + 4 * (S::kInsts * wave + i) * kRowBytes);
+      }
+    } else {
+      const unsigned bytes = (unsigned)(end - key0) * kRowBytes;
+      const u32x4 rk = buffer_rsrc(Kg + (size_t)key0 * kD, bytes);
+      const u32x4 rv = buffer_rsrc(Vg + (size_t)key0 * kD, bytes);
 #pragma unroll
-    for (int i = 0; i < S::kInsts; ++i)
-      dma_load_x4(ld_off[1][i], rv, lds_v0 + slot * S::kStepBytes + 4 * (S::kInsts * wave + i) * kRowBytes);
+      for (int i = 0; i < S::kInsts; ++i)
+        dma_load_x4(ld_off[0][i], rk, lds_k0 + slot * S::kStepBytes + 4 * (S::kInsts * wave + i) * kRowBytes);
+#pragma unroll
+      for (int i = 0; i < S::kInsts; ++i)
+        dma_load_x4(ld_off[1][i], rv, lds_v0 + slot * S::kStepBytes + 4 * (S::kInsts * wave + i) * kRowBytes);
+    }
   };
 
   f32x16 o[4];
@@ -473,18 +510,25 @@ int decode_multi_row_groups(int M) { return M <= 32 ? 1 : (M <= 64 ? 2 : 4); }
 hipError_t launch_decode_multi(const DecodeParams& p, hipStream_t stream, int phases) {
   if (phases & kDecodePartial) {
     const dim3 grid(p.n_split_max, p.H_kv, p.B);
+    const bool paged = p.block_table != nullptr;
     switch (decode_multi_row_groups(p.G * p.T_q)) {
       case 1:
-        hipLaunchKernelGGL(decode_multi_partial_kernel<1>, grid, dim3(MqLaunch<1>::S::kThreads), 0,
-                           stream, p);
+        if (paged)
+          hipLaunchKernelGGL((decode_multi_partial_kernel<1, true>), grid, dim3(MqLaunch<1>::S::kThreads), 0, stream, p);
+        else
+          hipLaunchKernelGGL((decode_multi_partial_kernel<1, false>), grid, dim3(MqLaunch<1>::S::kThreads), 0, stream, p);
         break;
       case 2:
-        hipLaunchKernelGGL(decode_multi_partial_kernel<2>, grid, dim3(MqLaunch<2>::S::kThreads), 0,
-                           stream, p);
+        if (paged)
+          hipLaunchKernelGGL((decode_multi_partial_kernel<2, true>), grid, dim3(MqLaunch<2>::S::kThreads), 0, stream, p);
+        else
+          hipLaunchKernelGGL((decode_multi_partial_kernel<2, false>), grid, dim3(MqLaunch<2>::S::kThreads), 0, stream, p);
         break;
       default:
-        hipLaunchKernelGGL(decode_multi_partial_kernel<4>, grid, dim3(MqLaunch<4>::S::kThreads), 0,
-                           stream, p);
+        if (paged)
+          hipLaunchKernelGGL((decode_multi_partial_kernel<4, true>), grid, dim3(MqLaunch<4>::S::kThreads), 0, stream, p);
+        else
+          hipLaunchKernelGGL((decode_multi_partial_kernel<4, false>), grid, dim3(MqLaunch<4>::S::kThreads), 0, stream, p);
         break;
     }
     const hipError_t e = hipGetLastError();

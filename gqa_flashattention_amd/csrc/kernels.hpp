@@ -23,6 +23,13 @@ struct DecodeParams {
   int n_split_max;      // ceil(max_kv_len / chunk)
   int q_negate;         // multi-token path: 1 when the scale is negative (Q's sign is flipped)
   float scale_log2;     // scale * log2(e); |scale| * log2(e) on the multi-token path
+  // Paged cache (block_table non-null): k, v are [num_pages, H_kv, page, d]
+  // pools; position j of sequence b is row j % page of physical page
+  // block_table[b * max_pages + j / page]; page = 1 << page_shift.
+  const int32_t* block_table;
+  int max_pages;
+  int page_shift;
+  int num_pages;        // pool size; table entries are clamped into [0, num_pages)
 };
 
 struct PrefillParams {

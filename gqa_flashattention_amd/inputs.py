@@ -41,6 +41,7 @@ class Workload:
     causal: bool = True
     offset: int = 0      # prefill: cached tokens before the chunk
     T_q: int = 1         # decode_multi: new tokens per sequence (the last T_q positions)
+    page_size: int = 0   # decode_paged: positions per page of the paged cache
 
     @property
     def G(self) -> int:
@@ -117,6 +118,11 @@ WORKLOADS = {
     "decode_multi_llama70b_32k_t2": Workload("decode_multi_llama70b_32k_t2", "decode_multi",
                                              B=1, H_q=64, H_kv=8, d=128, dtype="bf16",
                                              lens=(32768,), kv_cap=32768, T_q=2),
+    # The decode_llama70b_32k cache in a pool of 64-position pages placed in
+    # a seeded random order (T_q = 1).
+    "decode_paged_llama70b_32k_p64": Workload("decode_paged_llama70b_32k_p64", "decode_paged",
+                                              B=1, H_q=64, H_kv=8, d=128, dtype="bf16",
+                                              lens=(32768,), kv_cap=32768, T_q=1, page_size=64),
 }
 
 # Seed per workload: 20260000 + its position in the list above (1-based).
@@ -160,6 +166,43 @@ def make_decode_multi(w: Workload, device="cpu", seed=None, nan_pad=True, lens=N
     seed = SEEDS.get(w.name, 1) if seed is None else seed
     x["q"] = randn((w.B, w.H_q, w.T_q, w.d), w.torch_dtype, device, seed, 3)
     return x
+
+
+def make_decode_paged(w: Workload, page_size: int, device="cpu", seed=None, spare_pages=3):
+    """Paged-cache decode inputs: the contiguous inputs of ``make_decode_multi``
+    (same seeds, so the same values) scattered into a pool of pages.
+
+    Pages are ``[num_pages, H_kv, page_size, d]``; each sequence's logical
+    pages take physical pages in a seeded random order, and ``spare_pages``
+    extra pages are filled with NaN.  Table entries past a sequence's pages
+    name a NaN page (never a page out of range), and rows of a last page
+    past the sequence's length are NaN, so a kernel that reads them poisons
+    its output.  Returns q, k_pages, v_pages, block_table ``[B, max_pages]``
+    int32, kv_lens int32 and the contiguous k, v.
+    """
+    x = make_decode_multi(w, device=device, seed=seed)
+    seed = SEEDS.get(w.name, 1) if seed is None else seed
+    max_pages = (w.kv_cap + page_size - 1) // page_size
+    need = [(L + page_size - 1) // page_size for L in w.lens]
+    num_pages = sum(need) + spare_pages
+    g = torch.Generator().manual_seed(seed * 16 + 4)
+    perm = torch.randperm(num_pages, generator=g)
+    nan_page = int(perm[-1])
+    table = torch.full((w.B, max_pages), nan_page, dtype=torch.int32)
+    k_pages = torch.full((num_pages, w.H_kv, page_size, w.d), float("nan"), dtype=w.torch_dtype,
+                         device=device)
+    v_pages = torch.full_like(k_pages, float("nan"))
+    nxt = 0
+    for b, L in enumerate(w.lens):
+        for lp in range(need[b]):
+            pp = int(perm[nxt])
+            nxt += 1
+            table[b, lp] = pp
+            rows = min(page_size, L - lp * page_size)
+            k_pages[pp, :, :rows] = x["k"][b, :, lp * page_size:lp * page_size + rows]
+            v_pages[pp, :, :rows] = x["v"][b, :, lp * page_size:lp * page_size + rows]
+    return {"q": x["q"], "k_pages": k_pages, "v_pages": v_pages,
+            "block_table": table.to(device), "kv_lens": x["kv_lens"], "k": x["k"], "v": x["v"]}
 
 
 def make_prefill(w: Workload, device="cpu", seed=None, nan_pad=True, kv_cap=None):

@@ -11,6 +11,8 @@
  *   gqa_attn_prefill  a chunk of S_q query tokens, optionally causal with an
  *                     offset (the chunk follows causal_offset cached tokens).
  *   gqa_attn_merge    stitches two (O, lse) results over disjoint key sets.
+ *   gqa_attn_decode_paged
+ *                     decode (T_q >= 1) over a paged K/V cache (block table).
  *   gqa_attn_decode_multi
  *                     T_q >= 1 new tokens per sequence (speculative or
  *                     short-chunk decode) against the cache that holds them:
@@ -236,6 +238,64 @@ int gqa_attn_decode_multi_combine(const void* q, const void* k_cache, const void
                                   int H_q, int H_kv, int d, int T_q, int kv_cap,
                                   int max_kv_len, float scale, int dtype, int chunk_tokens,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode (T_q >= 1 new tokens per sequence, as gqa_attn_decode_multi; T_q = 1
+ * is plain decode) over a paged K/V cache.
+ *
+ *   k_pages, v_pages [num_pages, H_kv, page_size, d] bf16: a pool of pages,
+ *            each holding page_size consecutive positions of every KV head.
+ *   block_table [B, max_pages_per_seq] int32, DEVICE memory: position j of
+ *            sequence b is row j % page_size of page block_table[b][j /
+ *            page_size].  Entries for pages past a sequence's length are
+ *            never read.  Contract (not checked): entries lie in
+ *            [0, num_pages); an entry outside is read as the nearest end of
+ *            that range (wrong values, no memory outside the pool is read).
+ *   kv_lens, q, o, lse, max_kv_len, scale, chunk_tokens, workspace: as for
+ *            gqa_attn_decode_multi; rows of a sequence's last page past its
+ *            length are never read.
+ *   page_size  a power of two in [16, 65536]; max_pages_per_seq * page_size
+ *            >= max_kv_len.
+ *
+ * The same two launches as gqa_attn_decode_multi (the split kernel for the
+ * fold's size, then the combine); the split kernels address each 16-key
+ * sub-block (decode kernel) or 4-row load (multi-token kernel) in its own
+ * page, so pages need no particular placement in the pool.  Splits are
+ * capped so that one wave range spans at most 64 pages (G*T_q <= 16) or one
+ * split at most 128 pages (larger folds): an explicit chunk_tokens above
+ * that is GQA_ERR_INVALID_ARG.  Requirements as for gqa_attn_decode_multi
+ * (bf16, d == 128, G*T_q <= 128).
+ */
+int gqa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, const int32_t* kv_lens, void* o,
+                          float* lse, int B, int H_q, int H_kv, int d, int T_q, int page_size,
+                          int max_pages_per_seq, int num_pages, int max_kv_len, float scale,
+                          int dtype, int chunk_tokens, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Its two launches separately, as gqa_attn_decode_partial / _combine are for
+ * decode: same arguments and validation; _partial then _combine on one
+ * stream is gqa_attn_decode_paged. */
+int gqa_attn_decode_paged_partial(const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* block_table, const int32_t* kv_lens, void* o,
+                                  float* lse, int B, int H_q, int H_kv, int d, int T_q,
+                                  int page_size, int max_pages_per_seq, int num_pages,
+                                  int max_kv_len, float scale, int dtype, int chunk_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+int gqa_attn_decode_paged_combine(const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* block_table, const int32_t* kv_lens, void* o,
+                                  float* lse, int B, int H_q, int H_kv, int d, int T_q,
+                                  int page_size, int max_pages_per_seq, int num_pages,
+                                  int max_kv_len, float scale, int dtype, int chunk_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Keys per split and workspace bytes of gqa_attn_decode_paged (negative
+ * status / 0 on invalid arguments, as for the other sizing queries). */
+int gqa_attn_decode_paged_split_tokens(int B, int H_q, int H_kv, int T_q, int page_size,
+                                       int max_kv_len, int chunk_tokens, int dtype);
+size_t gqa_attn_decode_paged_workspace_bytes(int B, int H_q, int H_kv, int d, int T_q,
+                                             int page_size, int max_kv_len, int chunk_tokens,
+                                             int dtype);
 
 /*
  * Stitching of two attention results for the same query rows over disjoint

@@ -209,3 +209,45 @@ def _merge(**kw):
 ])
 def test_merge_rejects_before_launch(kw, status):
     assert _merge(**kw) == status
+
+
+def _paged(**kw):
+    a = dict(q=P, kp=P, vp=P, bt=P2, lens=P2, o=P, lse=None, B=1, H_q=8, H_kv=1, d=128, T_q=1,
+             page=64, maxp=4, npages=4, maxlen=256, scale=0.088, dtype=BF16, chunk=0, ws=P2,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return binding.lib().gqa_attn_decode_paged(
+        a["q"], a["kp"], a["vp"], a["bt"], a["lens"], a["o"], a["lse"], a["B"], a["H_q"],
+        a["H_kv"], a["d"], a["T_q"], a["page"], a["maxp"], a["npages"], a["maxlen"], a["scale"],
+        a["dtype"], a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), INVALID),
+    (dict(kp=None), INVALID),
+    (dict(bt=ctypes.c_void_p(0x200002)), INVALID),       # misaligned table
+    (dict(page=48), INVALID),                            # not a power of two
+    (dict(page=8), INVALID),                             # below 16
+    (dict(maxp=3), INVALID),                             # 3 * 64 < max_kv_len
+    (dict(npages=0), INVALID),
+    (dict(T_q=300, H_q=1), INVALID),                     # T_q > max_kv_len
+    (dict(chunk=64), INVALID),                           # not a multiple of 128
+    (dict(page=16, maxp=16, chunk=4096, maxlen=256), INVALID),   # a wave range over 64 pages
+    (dict(dtype=F32), UNSUPPORTED),
+    (dict(d=64), UNSUPPORTED),
+    (dict(T_q=17), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE),
+])
+def test_decode_paged_rejects_before_launch(kw, status):
+    assert _paged(**kw) == status
+
+
+def test_paged_split_rules():
+    L = binding.lib()
+    # Folds of <= 16 rows take the decode rule; larger folds the multi-token
+    # rule, capped at 127 pages per split.
+    assert L.gqa_attn_decode_paged_split_tokens(1, 64, 8, 1, 64, 32768, 0, BF16) == 512
+    assert L.gqa_attn_decode_paged_split_tokens(1, 64, 8, 4, 64, 32768, 0, BF16) == 1024
+    assert L.gqa_attn_decode_paged_split_tokens(1, 64, 8, 4, 16, 131072, 0, BF16) == 1920
+    assert L.gqa_attn_decode_paged_split_tokens(1, 64, 8, 4, 16, 131072, 2048, BF16) == -INVALID
+    assert L.gqa_attn_decode_paged_split_tokens(1, 64, 8, 4, 24, 131072, 0, BF16) == -INVALID
