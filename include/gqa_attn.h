@@ -176,7 +176,7 @@ int gqa_attn_decode_combine(const void* q, const void* k_cache,
  *   q        [B, H_q, T_q, d]        bf16: token t of each head is at
  *            position kv_lens[b] - T_q + t of its sequence.
  *   k_cache, v_cache [B, H_kv, kv_cap, d] bf16, read-only, already holding
- *            the T_q new tokens' rows (precondition P4 of §0.5.1).
+ *            the T_q new tokens' rows (precondition P3 of §0.5.1).
  *   kv_lens  [B] int32, DEVICE memory: valid length L of each sequence,
  *            new tokens included.  Token t sees keys 0 .. L - T_q + t (a
  *            causal tail: the last T_q - 1 keys are hidden from the earlier

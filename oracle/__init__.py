@@ -26,6 +26,7 @@ from .attention import (  # noqa: F401
     decode_paged,
     paged_gather,
     prefill,
+    prefill_varlen,
     prefill_visible_len,
     kv_head_of,
     partial,

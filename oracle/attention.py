@@ -114,7 +114,7 @@ def decode_multi_visible_len(L: int, G: int, T_q: int):
 
     The ``T_q`` new tokens of a sequence of ``L`` valid positions are its last
     ``T_q`` positions (their K/V rows are already in the cache, precondition
-    P4 of ADR-0060@5a76ed4 §0.5.1), so the query block starts at
+    P3 of ADR-0060@5a76ed4 §0.5.1), so the query block starts at
     ``q_start = L - T_q`` (``q_block_meta``, §0.5.3) and token ``t`` sees keys
     ``j <= q_start + t``.  The G query heads are stacked head by head,
     ``[G, T_q] -> [G*T_q]`` (§3 running state, §5.2): row ``r`` is token
@@ -152,6 +152,40 @@ def decode_multi(q, k_cache, v_cache, kv_lens, scale: float):
             ob, lb = attend_rows(rows, k_cache[b, kv, :L], v_cache[b, kv, :L], scale, vl)
             o[b, heads] = ob.reshape(G, T_q, d)
             lse[b, heads] = lb.reshape(G, T_q)
+    return o, lse
+
+
+def prefill_varlen(q, k, v, cu_seqlens_q, kv_lens, scale: float, causal: bool = True):
+    """A batch of prefill chunks of different lengths (token-packed).
+
+    q: ``[total_q, H_q, d]`` with sequence ``b``'s chunk at rows
+    ``cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1``; k, v: ``[B, H_kv, kv_cap, d]``
+    with ``kv_lens[b]`` valid positions.  Each chunk is the last ``S_q_b``
+    positions of its sequence (its K/V already in the cache, precondition P3
+    of ADR-0060@5a76ed4 §0.5.1), so with a causal mask its token ``i`` sees
+    keys ``j <= kv_lens[b] - S_q_b + i`` -- ``prefill`` with
+    ``causal_offset = kv_lens[b] - S_q_b`` (``q_block_meta``, §0.5.3); without
+    one, all ``kv_lens[b]`` keys.  Returns ``(o [total_q, H_q, d],
+    lse [total_q, H_q])``.
+    """
+    q = np.asarray(q)
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64).reshape(-1)
+    lens = np.asarray(kv_lens, dtype=np.int64).reshape(-1)
+    total, H_q, d = q.shape
+    o = np.empty((total, H_q, d), dtype=np.float64)
+    lse = np.empty((total, H_q), dtype=np.float64)
+    for b in range(len(cu) - 1):
+        t0, t1, L = int(cu[b]), int(cu[b + 1]), int(lens[b])
+        S_q = t1 - t0
+        if S_q == 0:
+            continue
+        if causal and S_q > L:
+            raise ValueError("a causal chunk must be the last S_q of its sequence's positions")
+        qb = np.transpose(q[t0:t1], (1, 0, 2))[None]            # [1, H_q, S_q, d]
+        ob, lb = prefill(qb, k[b:b + 1], v[b:b + 1], L, scale, causal=causal,
+                         causal_offset=L - S_q)
+        o[t0:t1] = np.transpose(ob[0], (1, 0, 2))
+        lse[t0:t1] = lb[0].T
     return o, lse
 
 

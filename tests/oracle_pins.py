@@ -448,6 +448,47 @@ def pin_paged_gather_round_trip(O):
         _close(lse, rl, what="paged decode lse")
 
 
+
+# ------------------------------------------------------------- varlen prefill
+
+def pin_prefill_varlen(O):
+    """A ragged batch of causal chunks against brute force per token (token i
+    of a chunk of S_q at the end of L positions sees keys 0 .. L - S_q + i);
+    an empty chunk is allowed; equal chunk lengths reduce to the multi-token
+    decode (whose rows are M-folded head by head, not token-packed); the
+    non-causal form sees every key."""
+    rng = _rng(30)
+    H_q, H_kv, d = 4, 2, 4
+    G = H_q // H_kv
+    seq = [(3, 7), (0, 4), (5, 5), (1, 9)]          # (S_q, L) per sequence
+    cap = 10
+    cu = np.concatenate([[0], np.cumsum([sq for sq, _ in seq])])
+    q = rng.standard_normal((int(cu[-1]), H_q, d))
+    k = rng.standard_normal((len(seq), H_kv, cap, d))
+    v = rng.standard_normal((len(seq), H_kv, cap, d))
+    lens = np.array([L for _, L in seq])
+    o, lse = O.prefill_varlen(q, k, v, cu, lens, 0.8, causal=True)
+    for b, (sq, L) in enumerate(seq):
+        for i in range(sq):
+            for h in range(H_q):
+                top = L - sq + i + 1
+                ro, rl = _mp_attention(q[cu[b] + i, h], k[b, h // G, :top], v[b, h // G, :top], 0.8)
+                _close(o[cu[b] + i, h], ro, what="varlen brute o")
+                _close(lse[cu[b] + i, h], rl, what="varlen brute lse")
+    onc, _ = O.prefill_varlen(q, k, v, cu, lens, 0.8, causal=False)
+    for b, (sq, L) in enumerate(seq):
+        for i in range(sq):
+            ro, _ = _mp_attention(q[cu[b] + i, 1], k[b, 0, :L], v[b, 0, :L], 0.8)
+            _close(onc[cu[b] + i, 1], ro, what="varlen non-causal")
+    T_q, lens2 = 3, np.array([3, 8])
+    q2 = rng.standard_normal((2, H_q, T_q, d))
+    packed = np.transpose(q2, (0, 2, 1, 3)).reshape(2 * T_q, H_q, d)
+    o2, l2 = O.prefill_varlen(packed, k[:2], v[:2], np.array([0, 3, 6]), lens2, 0.5)
+    om, lm = O.decode_multi(q2, k[:2], v[:2], lens2, 0.5)
+    _close(o2, np.transpose(om, (0, 2, 1, 3)).reshape(2 * T_q, H_q, d), what="varlen == multi decode")
+    _close(l2, np.transpose(lm, (0, 2, 1)).reshape(2 * T_q, H_q), what="varlen lse == multi decode")
+
+
 PINS = [
     pin_brute_force_decode,
     pin_brute_force_prefill,
@@ -468,4 +509,5 @@ PINS = [
     pin_decode_multi_special_cases,
     pin_merge_normalized_chunks,
     pin_paged_gather_round_trip,
+    pin_prefill_varlen,
 ]

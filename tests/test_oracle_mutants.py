@@ -44,6 +44,9 @@ MUTANTS = {
                         "out[b, :, j] = pages[table[b, j // page_size], :, (j + 1) % page_size]"),
     "paged_wrong_page": ("out[b, :, j] = pages[table[b, j // page_size], :, j % page_size]",
                          "out[b, :, j] = pages[table[b, j % page_size], :, j % page_size]"),
+    "varlen_offset_zero": ("causal_offset=L - S_q)\n        o[t0:t1]", "causal_offset=0)\n        o[t0:t1]"),
+    "varlen_heads_tokens_swapped": ("qb = np.transpose(q[t0:t1], (1, 0, 2))[None]",
+                                    "qb = q[t0:t1].reshape(q.shape[1], t1 - t0, q.shape[2])[None]"),
     "visible_ignored": ("vis = np.arange(j0, j1)[None, :] < vl[:, None]",
                         "vis = np.arange(j0, j1)[None, :] < L + 0 * vl[:, None]"),
 }
