@@ -51,7 +51,9 @@ def parse():
     ap.add_argument("--decode-workload", default="decode_llama70b_32k",
                     help="decode workload name (the headline is decode_llama70b_32k; "
                          "decode_multi_* workloads run gqa_attn_decode_multi)")
-    ap.add_argument("--prefill-workload", default="prefill_causal_8k")
+    ap.add_argument("--prefill-workload", default="prefill_causal_8k",
+                    help="prefill workload name (prefill_varlen_* workloads run "
+                         "gqa_attn_prefill_varlen)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of each oracle sample")
@@ -156,6 +158,36 @@ def cpu_baseline_prefill(w, x_cpu, seconds):
                       f"numpy fp64"}
 
 
+def cpu_baseline_prefill_varlen(w, x_cpu, seconds):
+    """Oracle on seeded query rows of every chunk of a varlen batch (all 64
+    heads), taken round-robin over the sequences in blocks of up to 16 rows
+    until ~seconds of CPU time; FLOPs counted exactly per row."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(7)
+    cu = np.concatenate([[0], np.cumsum(w.q_lens)])
+    orders = [rng.permutation(sq) for sq in w.q_lens]
+    q, k, v = (x_cpu[n] for n in ("q", "k", "v"))
+    done, flops, pos, t0 = 0, 0, [0] * w.B, time.perf_counter()
+    while time.perf_counter() - t0 < seconds and done < w.total_q:
+        for b, (sq, L) in enumerate(zip(w.q_lens, w.lens)):
+            if pos[b] >= sq:
+                continue
+            rows = np.sort(orders[b][pos[b]:pos[b] + 16])
+            pos[b] += len(rows)
+            qb = np.transpose(q[cu[b]:cu[b + 1]], (1, 0, 2))[None]
+            oracle.prefill(qb, k[b:b + 1], v[b:b + 1], L, w.scale, causal=w.causal,
+                           causal_offset=L - sq, rows=rows)
+            vis = oracle.prefill_visible_len(rows, L, w.causal, L - sq)
+            flops += 4 * w.d * w.H_q * int(vis.sum())
+            done += len(rows)
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"{done} seeded query rows (up to 16 per chunk per round) x {w.H_q} heads "
+                      f"of {w.name} in {el:.1f} s, numpy fp64"}
+
+
 def bench_merge(args):
     """gqa_attn_merge on two results of the prefill_causal_8k shape: rows =
     64 heads x 8192 positions, O bf16 [rows, 128], LSE float32.  HBM bound:
@@ -225,6 +257,7 @@ def main():
     multi = wd.kind in ("decode_multi", "decode_paged")
     paged = wd.kind == "decode_paged"
     wp = inputs.WORKLOADS[args.prefill_workload]
+    varlen = wp.kind == "prefill_varlen"
     do_dec = args.only in ("decode", "both")
     do_pre = args.only in ("prefill", "both")
 
@@ -257,11 +290,16 @@ def main():
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         o_dec = torch.empty_like(copies[0]["q"])
     if do_pre:
-        xp = inputs.make_prefill(wp, device=dev)
+        xp = (inputs.make_prefill_varlen if varlen else inputs.make_prefill)(wp, device=dev)
         o_pre = torch.empty_like(xp["q"])
     torch.cuda.synchronize()
 
     def prefill_call():
+        if varlen:
+            gq.prefill_varlen(xp["q"], xp["k"], xp["v"], xp["cu_seqlens_q"], xp["kv_lens"],
+                              max_seqlen_q=max(wp.q_lens), max_kv_len=wp.max_kv_len,
+                              causal=wp.causal, scale=wp.scale, out=o_pre, stream=stream)
+            return
         gq.prefill(xp["q"], xp["k"], xp["v"], S_kv=wp.S_kv, causal=wp.causal,
                    causal_offset=wp.offset, scale=wp.scale, out=o_pre, stream=stream)
 
@@ -346,9 +384,13 @@ def main():
                               "gqa_attn_decode_multi" if multi else "gqa_attn_decode",
                               "kv_lens": list(wd.lens), "kv_copies": len(copies) if do_dec else 0,
                               "keys_per_split": chunk if do_dec else None},
-                   "prefill": {"B": wp.B, "H_q": wp.H_q, "H_kv": wp.H_kv, "d": wp.d,
-                               "S_q": wp.S_q, "S_kv": wp.S_kv, "causal": wp.causal,
-                               "offset": wp.offset}},
+                   "prefill": ({"B": wp.B, "H_q": wp.H_q, "H_kv": wp.H_kv, "d": wp.d,
+                                "entry_point": "gqa_attn_prefill_varlen",
+                                "q_lens": list(wp.q_lens), "kv_lens": list(wp.lens),
+                                "causal": wp.causal} if varlen else
+                               {"B": wp.B, "H_q": wp.H_q, "H_kv": wp.H_kv, "d": wp.d,
+                                "S_q": wp.S_q, "S_kv": wp.S_kv, "causal": wp.causal,
+                                "offset": wp.offset})},
         "wall_s_timed_region": round(wall, 4),
     }
     if do_dec:
@@ -386,7 +428,8 @@ def main():
         out["prefill"] = {"value": round(tf, 2), "unit": "TFLOP/s",
                           "ms_mean": round(mean(pre_ms), 6), "ms_median": round(median(pre_ms), 6),
                           "flops_per_call": wp.prefill_flops(),
-                          "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel",
+                          "roofline": {"bound": "mfma",
+                                       "kernel": f"prefill_bf16_kernel<{str(varlen).lower()}>",
                                        "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                                        "traffic": traffic_from_profiles("prefill", wp.name),
@@ -407,7 +450,8 @@ def main():
             del xc
         if do_pre:
             xc = {n: xp[n].float().cpu().numpy() for n in ("q", "k", "v")}
-            out["prefill"]["cpu_baseline"] = cpu_baseline_prefill(wp, xc, args.cpu_seconds)
+            fn = cpu_baseline_prefill_varlen if varlen else cpu_baseline_prefill
+            out["prefill"]["cpu_baseline"] = fn(wp, xc, args.cpu_seconds)
             del xc
 
     print(json.dumps(out), flush=True)

@@ -38,6 +38,9 @@ SIGNATURES = {
                                      _i, _i, _vp, _sz, _vp]),
     "gqa_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                               _f, _i, _vp]),
+    "gqa_attn_prefill_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                     _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "gqa_attn_prefill_varlen_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "gqa_attn_merge": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_longlong, _i, _i, _vp]),
     "gqa_attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                    _i, _i, _f, _i, _i, _vp, _sz, _vp]),
@@ -317,4 +320,50 @@ def prefill(q, k, v, S_kv=None, causal=True, causal_offset=0, scale=None, return
                                 kv_cap, int(bool(causal)), int(causal_offset), scale, dt,
                                 _stream(stream))
     _check(st, "gqa_attn_prefill")
+    return (out, lse) if return_lse else out
+
+
+def prefill_varlen_workspace_bytes(B, H_q, H_kv, max_seqlen_q) -> int:
+    return int(lib().gqa_attn_prefill_varlen_workspace_bytes(B, H_q, H_kv, max_seqlen_q))
+
+
+def prefill_varlen(q, k, v, cu_seqlens_q, kv_lens, max_seqlen_q, max_kv_len=None, causal=True,
+                   scale=None, return_lse=False, out=None, lse=None, workspace=None,
+                   stream=None):
+    """``gqa_attn_prefill_varlen`` on torch tensors.
+
+    q ``[total_q,H_q,d]`` bf16 (sequence b's chunk at rows ``cu_seqlens_q[b]``
+    .. ``cu_seqlens_q[b+1]-1``, the newest positions of its cache),
+    k/v ``[B,H_kv,kv_cap,d]`` bf16, cu_seqlens_q ``[B+1]`` and kv_lens ``[B]``
+    int32 on the device.  ``max_seqlen_q`` bounds every chunk length and
+    ``max_kv_len`` (default ``kv_cap``) every cache length: both are host
+    values, so no device array is read back.  ``workspace`` (uint8 device
+    tensor, allocated when None) holds the work list.  Returns ``o`` (and
+    ``lse`` ``[total_q,H_q]`` when ``return_lse``).
+    """
+    _require_gpu(q, k, v, cu_seqlens_q, kv_lens)
+    total_q, H_q, d = q.shape
+    B, H_kv, kv_cap, _ = k.shape
+    if cu_seqlens_q.dtype != torch.int32 or kv_lens.dtype != torch.int32:
+        raise TypeError("cu_seqlens_q and kv_lens must be int32")
+    if cu_seqlens_q.numel() != B + 1 or kv_lens.numel() != B:
+        raise ValueError("cu_seqlens_q must hold B+1 entries and kv_lens B")
+    max_kv_len = kv_cap if max_kv_len is None else int(max_kv_len)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((total_q, H_q), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = prefill_varlen_workspace_bytes(B, H_q, H_kv, int(max_seqlen_q))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib().gqa_attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                                       _ptr(kv_lens), _ptr(out),
+                                       _ptr(lse) if return_lse else None, B, H_q, H_kv, d,
+                                       total_q, int(max_seqlen_q), kv_cap, max_kv_len,
+                                       int(bool(causal)), scale, dt, _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream))
+    _check(st, "gqa_attn_prefill_varlen")
     return (out, lse) if return_lse else out

@@ -134,7 +134,7 @@ const char* gqa_attn_status_string(int status) {
   }
 }
 
-int gqa_attn_version(void) { return 200; }
+int gqa_attn_version(void) { return 210; }
 
 int gqa_attn_decode_split_tokens(int B, int H_kv, int max_kv_len, int chunk_tokens, int dtype) {
   return split_tokens(B, H_kv, max_kv_len, chunk_tokens, dtype);
@@ -510,6 +510,72 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float
   p.n_qblk = (int)n_qblk;
   p.q_negate = scale < 0.f;
   p.scale_log2 = fabsf(scale) * 1.4426950408889634f;
+  p.cu_seqlens_q = nullptr;
+  p.kv_lens = nullptr;
+  p.sched = nullptr;
+  hipError_t e = gqa::launch_prefill(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+size_t gqa_attn_prefill_varlen_workspace_bytes(int B, int H_q, int H_kv, int max_seqlen_q) {
+  if (B < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || max_seqlen_q < 0) return 0;
+  const int hpw = gqa::prefill_heads_per_wg(H_q / H_kv);
+  const long long rows_per_wg = gqa::prefill_rows_per_wg() / hpw;
+  const long long n_qblk = ((long long)max_seqlen_q + rows_per_wg - 1) / rows_per_wg;
+  return gqa::prefill_varlen_sched_bytes(B, n_qblk);
+}
+
+int gqa_attn_prefill_varlen(const void* q, const void* k, const void* v, const int* cu_seqlens_q,
+                            const int* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
+                            int d, int total_q, int max_seqlen_q, int kv_cap, int max_kv_len,
+                            int causal, float scale, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !cu_seqlens_q || !kv_lens) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GQA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(cu_seqlens_q) |
+       reinterpret_cast<uintptr_t>(kv_lens)) & 3u)
+    return GQA_ERR_INVALID_ARG;
+  if (B < 1 || H_q < 1 || H_kv < 1 || d < 1 || total_q < 0 || kv_cap < 1)
+    return GQA_ERR_INVALID_ARG;
+  if (max_seqlen_q < 0 || max_seqlen_q > total_q) return GQA_ERR_INVALID_ARG;
+  if (max_kv_len < 1 || max_kv_len > kv_cap) return GQA_ERR_INVALID_ARG;
+  if (H_q % H_kv != 0) return GQA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16) return GQA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (d != kD || dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  if ((long long)total_q * H_q * kD >= (1LL << 62)) return GQA_ERR_INVALID_ARG;
+  if (max_seqlen_q == 0) return GQA_OK;
+  const int hpw = gqa::prefill_heads_per_wg(H_q / H_kv);
+  const long long rows_per_wg = gqa::prefill_rows_per_wg() / hpw;
+  const long long n_qblk = ((long long)max_seqlen_q + rows_per_wg - 1) / rows_per_wg;
+  if (n_qblk * B * H_kv * ((H_q / H_kv) / hpw) > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      workspace_bytes < gqa::prefill_varlen_sched_bytes(B, n_qblk))
+    return GQA_ERR_WORKSPACE;
+
+  gqa::PrefillParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H_q = H_q;
+  p.H_kv = H_kv;
+  p.G = H_q / H_kv;
+  p.S_q = total_q;
+  p.S_kv = max_kv_len;
+  p.kv_cap = kv_cap;
+  p.causal = causal;
+  p.offset = 0;
+  p.heads_per_wg = hpw;
+  p.n_qblk = (int)n_qblk;
+  p.q_negate = scale < 0.f;
+  p.scale_log2 = fabsf(scale) * 1.4426950408889634f;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.kv_lens = kv_lens;
+  p.sched = static_cast<int*>(workspace);
   hipError_t e = gqa::launch_prefill(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }

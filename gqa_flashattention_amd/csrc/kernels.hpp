@@ -44,6 +44,14 @@ struct PrefillParams {
   int n_qblk;           // position blocks: ceil(S_q / (32 * waves / heads_per_wg))
   int q_negate;         // 1 when the softmax scale is negative (Q's sign is flipped)
   float scale_log2;     // |scale| * log2(e)
+  // Varlen batch (both null otherwise): q/o are [S_q = total_q, H_q, d],
+  // lse [total_q, H_q]; sequence b's chunk is rows cu_seqlens_q[b] ..
+  // cu_seqlens_q[b+1]-1 against min(kv_lens[b], S_kv) keys, causal offset
+  // (keys) - (chunk length); n_qblk covers the longest chunk.  `sched`
+  // holds B * n_qblk ints: the work list the varlen launch builds first.
+  const int* cu_seqlens_q;
+  const int* kv_lens;
+  int* sched;
 };
 
 struct MergeParams {
@@ -72,6 +80,10 @@ int decode_multi_row_groups(int M);
 // Query heads of one KV group a prefill workgroup covers, and the query rows
 // (heads x positions) of one workgroup.
 int prefill_heads_per_wg(int G);
+// Bytes of the varlen prefill work list for B sequences of n_qblk blocks.
+inline size_t prefill_varlen_sched_bytes(long long B, long long n_qblk) {
+  return (size_t)(((B * n_qblk * 4) + 255) / 256 * 256);
+}
 int prefill_rows_per_wg();
 
 }  // namespace gqa

@@ -43,6 +43,16 @@
 // round-robin dispatch of workgroups over the 8 XCDs each KV head's tiles
 // stay in one XCD's L2; query blocks go heaviest (longest causal prefix)
 // first.
+//
+// Varlen batches (chunks of several sequences in one launch, each the newest
+// positions of its sequence): the same kernel, with each workgroup reading
+// its sequence's chunk length and key count and taking the causal offset
+// (keys) - (chunk length), q_block_meta of §0.5.3 per sequence.  The
+// lengths live on the device, so a one-workgroup pre-pass sorts the
+// (sequence, position block) items by their tile count (a counting sort in
+// LDS) into a work list, heaviest first, and workgroup i takes item i: a
+// long chunk over a long cache starts first instead of trailing the grid.
+// Items past a chunk's end cost nothing and sort last.
 
 #include <type_traits>
 
@@ -80,6 +90,11 @@ using Int = std::integral_constant<int, N>;
 
 }  // namespace
 
+// kVarlen: a batch of chunks of different lengths, token-packed.  Sequence
+// b's chunk is q/o rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of
+// [total_q, H_q, d] (lse [total_q, H_q]) against kv_lens[b] cached keys,
+// with causal offset kv_lens[b] - S_q_b; otherwise q/o are [B, H_q, S_q, d].
+template <bool kVarlen>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) __bf16 sK[kBufs][kTileElems];
   __shared__ __attribute__((aligned(1024))) __bf16 sV[kBufs][kTileElems];
@@ -93,9 +108,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   id /= p.H_kv;
   const int hg = id % ngroups;
   id /= ngroups;
-  const int b = id % p.B;
-  id /= p.B;
-  const int pblk = p.n_qblk - 1 - id;
+  int b, pblk;
+  if constexpr (kVarlen) {
+    // Work-list entry b * n_qblk + pblk, clamped into range.
+    const unsigned n_items = (unsigned)p.B * (unsigned)p.n_qblk;
+    const unsigned item = min((unsigned)p.sched[id], n_items - 1u);
+    b = (int)(item / (unsigned)p.n_qblk);
+    pblk = (int)(item % (unsigned)p.n_qblk);
+  } else {
+    b = id % p.B;
+    id /= p.B;
+    pblk = p.n_qblk - 1 - id;
+  }
 
   const int t = threadIdx.x;
   const int wave = t >> 6;
@@ -110,20 +134,54 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int qw0 = P0 + 32 * (wave / hpw);   // first row of this wave
   const int qrow = qw0 + c;                 // this lane's query row
 
-  int kend = p.S_kv;
-  if (p.causal) kend = min(kend, p.offset + P0 + 32 * pbw);
+  // This sequence's chunk length, key count and causal offset; query row i
+  // of head h is row `qrow0 + i * qstride` of the [rows, d] view of q, o
+  // and lse.  Varlen sizes come from device arrays and are clamped, so a
+  // malformed array cannot move any access outside the buffers (it only
+  // makes the results meaningless).
+  int S_q, S_kv, offset, qstride;
+  size_t qrow0;
+  if constexpr (kVarlen) {
+    const int t0 = min(max(p.cu_seqlens_q[b], 0), p.S_q);
+    const int t1 = min(max(p.cu_seqlens_q[b + 1], t0), p.S_q);
+    S_q = t1 - t0;
+    S_kv = min(max(p.kv_lens[b], 0), p.S_kv);
+    offset = p.causal ? max(S_kv - S_q, 0) : 0;
+    qrow0 = (size_t)t0 * p.H_q + h;
+    qstride = p.H_q;
+  } else {
+    S_q = p.S_q;
+    S_kv = p.S_kv;
+    offset = p.offset;
+    qrow0 = ((size_t)b * p.H_q + h) * p.S_q;
+    qstride = 1;
+  }
+  if (P0 >= S_q) return;   // the whole workgroup: past this chunk's end
+  if (S_kv == 0) {
+    // No key (an empty sequence, varlen only): O = 0, lse = -inf, the
+    // convention for a row that sees nothing.
+    if (qrow < S_q) {
+      __bf16* orow = static_cast<__bf16*>(p.o) + (qrow0 + (size_t)qrow * qstride) * kD;
+      for (int d0 = 4 * h2; d0 < kD; d0 += 8)
+        *reinterpret_cast<u32x2*>(orow + d0) = u32x2{0, 0};
+      if (p.lse != nullptr && h2 == 0) p.lse[qrow0 + (size_t)qrow * qstride] = kNegInf;
+    }
+    return;
+  }
+
+  int kend = S_kv;
+  if (p.causal) kend = min(kend, offset + P0 + 32 * pbw);
   const int ntiles = (kend + kBN - 1) / kBN;
   // Tiles [0, n_full) need no mask for this wave, [n_full, n_live) are
   // masked (diagonal or past S_kv), the rest are invisible to all its rows.
   int n_live = ntiles;
-  int n_full = p.S_kv / kBN;
+  int n_full = S_kv / kBN;
   if (p.causal) {
-    n_live = min(ntiles, (p.offset + qw0 + 31) / kBN + 1);
-    n_full = min(n_full, (p.offset + qw0 + 1) / kBN);
+    n_live = min(ntiles, (offset + qw0 + 31) / kBN + 1);
+    n_full = min(n_full, (offset + qw0 + 1) / kBN);
   }
   n_full = min(n_full, n_live);
 
-  const __bf16* Q = static_cast<const __bf16*>(p.q) + ((size_t)b * p.H_q + h) * p.S_q * kD;
   const __bf16* Kg = static_cast<const __bf16*>(p.k) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
   const __bf16* Vg = static_cast<const __bf16*>(p.v) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
 
@@ -131,8 +189,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // scale is applied exactly by flipping Q's sign bits.
   bf16x8 qb[8];
   {
-    const bool ok = qrow < p.S_q;
-    const __bf16* qr = Q + (size_t)(ok ? qrow : 0) * kD + 8 * h2;
+    const bool ok = qrow < S_q;
+    const __bf16* qr =
+        static_cast<const __bf16*>(p.q) + (qrow0 + (size_t)(ok ? qrow : 0) * qstride) * kD + 8 * h2;
     const unsigned flip = p.q_negate ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -201,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   auto tile_load_part = [&](int kv, int buf, int tile, int i) {
     tile = min(tile, ntiles - 1);
     const u32x4 rsrc = buffer_rsrc((kv ? Vg : Kg) + (size_t)tile * (kBN * kD),
-                                   (unsigned)(p.S_kv - tile * kBN) * (kD * 2));
+                                   (unsigned)(S_kv - tile * kBN) * (kD * 2));
     dma_load_x4(ld_off[kv][i], rsrc,
                 (kv ? lds_v0 : lds_k0) + buf * kTileBytes + 4 * (kInsts * wave + i) * kD * 2);
   };
@@ -246,7 +305,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // still give -inf; for |scale * q.k| far below 2^-24 * 32 the weights are
   // the same as with the exact scale.
   const float sl2 = fmaxf(p.scale_log2, 1e-30f);
-  const int vis_last = p.causal ? p.offset + qrow : p.S_kv - 1;
+  const int vis_last = p.causal ? offset + qrow : S_kv - 1;
 
   auto mask_tile = [&](Tile16& T, int tile) {
     const int kbase = tile * kBN;
@@ -255,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kbase + 32 * mt + 8 * (i >> 2) + 4 * h2 + (i & 3);
-        if (key > vis_last || key >= p.S_kv) T.s[mt][i] = kNegInf;
+        if (key > vis_last || key >= S_kv) T.s[mt][i] = kNegInf;
       }
   };
 
@@ -447,9 +506,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // Epilogue: O = O / l, rounded to bf16.  Lane holds, for d-tile dt and
   // i = 0..15, d = 32*dt + 8*(i/4) + 4*h2 + (i%4) of row qrow.
   const float lsum = lpart + __shfl_xor(lpart, 32, 64);
-  if (qrow < p.S_q) {
+  if (qrow < S_q) {
     const float inv = 1.f / lsum;
-    __bf16* orow = static_cast<__bf16*>(p.o) + (((size_t)b * p.H_q + h) * p.S_q + qrow) * kD;
+    __bf16* orow = static_cast<__bf16*>(p.o) + (qrow0 + (size_t)qrow * qstride) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -460,7 +519,75 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
         *reinterpret_cast<u32x2*>(orow + d0) = v2;
       }
     if (p.lse != nullptr && h2 == 0)
-      p.lse[((size_t)b * p.H_q + h) * p.S_q + qrow] = (m_ref + __log2f(lsum)) * kLn2;
+      p.lse[qrow0 + (size_t)qrow * qstride] = (m_ref + __log2f(lsum)) * kLn2;
+  }
+}
+
+// Tile count of a varlen work item (b, pblk): the key tiles its workgroup
+// walks (0 past the chunk's end).  Mirrors the extent computed in the
+// attention kernel.
+__device__ __forceinline__ int varlen_item_cost(const PrefillParams& p, int item) {
+  const int b = item / p.n_qblk, pblk = item % p.n_qblk;
+  const int t0 = min(max(p.cu_seqlens_q[b], 0), p.S_q);
+  const int t1 = min(max(p.cu_seqlens_q[b + 1], t0), p.S_q);
+  const int S_q = t1 - t0;
+  const int S_kv = min(max(p.kv_lens[b], 0), p.S_kv);
+  const int rows = 32 * (kWaves / p.heads_per_wg);
+  const int P0 = pblk * rows;
+  if (P0 >= S_q) return 0;
+  int kend = S_kv;
+  if (p.causal) kend = min(kend, max(S_kv - S_q, 0) + P0 + rows);
+  return (kend + kBN - 1) / kBN;
+}
+
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedBins = 2048;
+
+// The varlen work list: every item b * n_qblk + pblk, ordered by tile count
+// (bins of 2^shift tiles), heaviest first.  One workgroup: histogram of the
+// bins in LDS, a descending exclusive scan, then each item placed at its
+// bin's cursor.  Items within a bin land in any order; the result of each
+// item does not depend on when it runs.
+__global__ __launch_bounds__(kSchedThreads) void prefill_varlen_schedule_kernel(PrefillParams p,
+                                                                               int* list,
+                                                                               int shift) {
+  __shared__ int hist[kSchedBins];
+  __shared__ int scan[kSchedThreads];
+  const int t = threadIdx.x;
+  const int n = p.B * p.n_qblk;
+  for (int i = t; i < kSchedBins; i += kSchedThreads) hist[i] = 0;
+  __syncthreads();
+  auto bin_of = [&](int item) { return min(varlen_item_cost(p, item) >> shift, kSchedBins - 1); };
+  for (int i = t; i < n; i += kSchedThreads) atomicAdd(&hist[bin_of(i)], 1);
+  __syncthreads();
+  // Descending order: thread t owns bins NB-1-2t and NB-2-2t.
+  constexpr int kPer = kSchedBins / kSchedThreads;
+  int local[kPer], sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    local[j] = hist[kSchedBins - 1 - (kPer * t + j)];
+    sum += local[j];
+  }
+  scan[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < kSchedThreads; off <<= 1) {   // inclusive Hillis-Steele scan
+    const int v = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
+  }
+  int base = scan[t] - sum;   // exclusive prefix of thread t's first bin
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    hist[kSchedBins - 1 - (kPer * t + j)] = base;   // becomes the bin's cursor
+    base += local[j];
+  }
+  __syncthreads();
+  // Both passes bin each item alike (the length arrays are read-only
+  // meanwhile), so every position is below n; the bound only guards the list.
+  for (int i = t; i < n; i += kSchedThreads) {
+    const int pos = atomicAdd(&hist[bin_of(i)], 1);
+    if (pos < n) list[pos] = i;
   }
 }
 
@@ -478,7 +605,19 @@ int prefill_rows_per_wg() { return 32 * kWaves; }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const long long nwg = (long long)p.n_qblk * p.B * p.H_kv * (p.G / p.heads_per_wg);
-  hipLaunchKernelGGL(prefill_bf16_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+  if (p.cu_seqlens_q != nullptr) {
+    int shift = 0;
+    while ((((long long)p.S_kv + kBN - 1) / kBN >> shift) >= kSchedBins) ++shift;
+    hipLaunchKernelGGL(prefill_varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, p,
+                       p.sched, shift);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                       p);
+  } else {
+    hipLaunchKernelGGL(prefill_bf16_kernel<false>, dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                       p);
+  }
   return hipGetLastError();
 }
 

@@ -42,6 +42,7 @@ class Workload:
     offset: int = 0      # prefill: cached tokens before the chunk
     T_q: int = 1         # decode_multi: new tokens per sequence (the last T_q positions)
     page_size: int = 0   # decode_paged: positions per page of the paged cache
+    q_lens: tuple = ()   # prefill_varlen: chunk length per sequence (lens: its cache length)
 
     @property
     def G(self) -> int:
@@ -61,7 +62,9 @@ class Workload:
 
     @property
     def max_kv_len(self) -> int:
-        return max(self.lens) if self.kind.startswith("decode") else self.S_kv
+        if self.kind.startswith("decode") or self.kind == "prefill_varlen":
+            return max(self.lens)
+        return self.S_kv
 
     def kv_bytes(self) -> int:
         """K+V bytes a decode step must read: valid keys only, padding excluded."""
@@ -88,7 +91,21 @@ class Workload:
 
     def prefill_flops(self) -> int:
         """Algorithmic FLOPs: 2*d for Q.K^T plus 2*d for P.V per visible pair."""
+        if self.kind == "prefill_varlen":
+            return 4 * self.d * self.H_q * self.varlen_visible_pairs()
         return 4 * self.d * self.B * self.H_q * self.visible_pairs_per_head()
+
+    def varlen_visible_pairs(self) -> int:
+        """(query, key) pairs per head of a varlen batch: chunk b (S_q tokens,
+        the newest of L positions) scores L - S_q + i + 1 keys for token i
+        when causal, L otherwise."""
+        if not self.causal:
+            return sum(sq * L for sq, L in zip(self.q_lens, self.lens))
+        return sum(sq * (L - sq) + sq * (sq + 1) // 2 for sq, L in zip(self.q_lens, self.lens))
+
+    @property
+    def total_q(self) -> int:
+        return sum(self.q_lens)
 
 
 WORKLOADS = {
@@ -123,6 +140,16 @@ WORKLOADS = {
     "decode_paged_llama70b_32k_p64": Workload("decode_paged_llama70b_32k_p64", "decode_paged",
                                               B=1, H_q=64, H_kv=8, d=128, dtype="bf16",
                                               lens=(32768,), kv_cap=32768, T_q=1, page_size=64),
+    # A chunked-prefill batch (continuous batching): eight sequences, each
+    # appending a chunk of a different length (a full 8K prompt, a long
+    # chunk over a 64K context, mid-size chunks, a ragged 37-token tail and
+    # a single decode-like token) to its own cache; 16166 query tokens.
+    "prefill_varlen_llama70b_b8": Workload("prefill_varlen_llama70b_b8", "prefill_varlen",
+                                           B=8, H_q=64, H_kv=8, d=128, dtype="bf16",
+                                           q_lens=(8192, 4096, 2048, 1024, 512, 256, 37, 1),
+                                           lens=(8192, 12288, 32768, 2048, 65536, 4096, 300,
+                                                 16384),
+                                           kv_cap=65536, causal=True),
 }
 
 # Seed per workload: 20260000 + its position in the list above (1-based).
@@ -217,6 +244,31 @@ def make_prefill(w: Workload, device="cpu", seed=None, nan_pad=True, kv_cap=None
         k[:, :, w.S_kv:].fill_(float("nan"))
         v[:, :, w.S_kv:].fill_(float("nan"))
     return {"q": q, "k": k, "v": v}
+
+
+def make_prefill_varlen(w: Workload, device="cpu", seed=None, nan_pad=True, q_lens=None,
+                        lens=None):
+    """Varlen prefill inputs: q ``[total_q,H_q,d]`` token-packed (chunk b at
+    rows ``cu_seqlens_q[b] ..``), k/v ``[B,H_kv,kv_cap,d]`` NaN past each
+    sequence's length, cu_seqlens_q ``[B+1]`` and kv_lens ``[B]`` int32."""
+    seed = SEEDS.get(w.name, 1) if seed is None else seed
+    q_lens = tuple(w.q_lens) if q_lens is None else tuple(q_lens)
+    lens = tuple(w.lens) if lens is None else tuple(lens)
+    dt = w.torch_dtype
+    cu = [0]
+    for sq in q_lens:
+        cu.append(cu[-1] + sq)
+    q = randn((cu[-1], w.H_q, w.d), dt, device, seed, 0)
+    k = randn((w.B, w.H_kv, w.kv_cap, w.d), dt, device, seed, 1)
+    v = randn((w.B, w.H_kv, w.kv_cap, w.d), dt, device, seed, 2)
+    if nan_pad:
+        for b, L in enumerate(lens):
+            if L < w.kv_cap:
+                k[b, :, L:].fill_(float("nan"))
+                v[b, :, L:].fill_(float("nan"))
+    return {"q": q, "k": k, "v": v,
+            "cu_seqlens_q": torch.tensor(cu, dtype=torch.int32, device=device),
+            "kv_lens": torch.tensor(lens, dtype=torch.int32, device=device)}
 
 
 def sample_rows(S_q: int, n: int, seed: int, always=(0, 1, 63, 64, 127, 128)):

@@ -10,6 +10,10 @@
  *                     merged by a log-sum-exp combine.
  *   gqa_attn_prefill  a chunk of S_q query tokens, optionally causal with an
  *                     offset (the chunk follows causal_offset cached tokens).
+ *   gqa_attn_prefill_varlen
+ *                     a batch of prefill chunks of different lengths
+ *                     (token-packed), each the newest positions of its
+ *                     sequence's cache.
  *   gqa_attn_merge    stitches two (O, lse) results over disjoint key sets.
  *   gqa_attn_decode_paged
  *                     decode (T_q >= 1) over a paged K/V cache (block table).
@@ -32,10 +36,12 @@
  *    the head dimension d innermost:
  *        q (decode)   [B, H_q, d]          q (prefill)  [B, H_q, S_q, d]
  *        q (decode_multi) [B, H_q, T_q, d]
+ *        q (prefill_varlen) [total_q, H_q, d] (token-packed chunks)
  *        k, v cache   [B, H_kv, kv_cap, d] (position j of a sequence = row j)
  *        o            same shape as q, same dtype as q
  *        lse          [B, H_q] (decode) / [B, H_q, S_q] (prefill) /
- *                     [B, H_q, T_q] (decode_multi), float32
+ *                     [B, H_q, T_q] (decode_multi) / [total_q, H_q]
+ *                     (prefill_varlen), float32
  *  - Query head h reads KV head h / (H_q / H_kv): the G = H_q / H_kv query
  *    heads sharing a KV head are adjacent.
  *  - Q and K are already RoPE-rotated, V is raw, and for decode the new
@@ -340,6 +346,55 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o,
                      float* lse, int B, int H_q, int H_kv, int d, int S_q,
                      int S_kv, int kv_cap, int causal, int causal_offset,
                      float scale, int dtype, void* stream);
+
+/*
+ * Varlen prefill: chunks of different lengths for B sequences in one launch
+ * (chunked prefill / continuous batching).  Each chunk is the newest S_q_b
+ * positions of its sequence, whose K/V rows are already in the cache
+ * (precondition P3 of §0.5.1), so its query block starts at
+ * q_start = kv_lens[b] - S_q_b (q_block_meta of §0.5.3), per sequence.
+ *
+ *   q     [total_q, H_q, d] bf16, token-packed: sequence b's chunk is rows
+ *         cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (token-major, heads inner)
+ *   cu_seqlens_q  [B+1] int32 DEVICE array, 4-byte aligned: 0 =
+ *         cu_seqlens_q[0] <= cu_seqlens_q[1] <= ... <= cu_seqlens_q[B] =
+ *         total_q; a sequence may have an empty chunk
+ *   k, v  [B, H_kv, kv_cap, d] bf16, read-only
+ *   kv_lens       [B] int32 DEVICE array, 4-byte aligned: valid positions
+ *         of each sequence's cache (the chunk included)
+ *   o     [total_q, H_q, d] bf16, written
+ *   lse   [total_q, H_q] float32, written when non-NULL
+ *   causal = 1: token i of chunk b sees keys j <= kv_lens[b] - S_q_b + i;
+ *           requires S_q_b <= kv_lens[b].
+ *   causal = 0: every token of chunk b sees all kv_lens[b] keys.
+ *   max_seqlen_q  an upper bound of every S_q_b (sizes the grid; rows past
+ *         it are not written); max_kv_len an upper bound of every kv_lens[b]
+ *         (kv_lens are clamped to it), 1 <= max_kv_len <= kv_cap.
+ *
+ * The device arrays are not read on the host: values outside the contract
+ * are clamped inside the kernel (no access leaves the buffers), but the
+ * results for such sequences are meaningless.  A sequence with
+ * kv_lens[b] = 0 and a non-empty chunk (non-causal) gets O = 0, lse = -inf.
+ *
+ *   workspace  DEVICE scratch of at least
+ *         gqa_attn_prefill_varlen_workspace_bytes(B, H_q, H_kv, max_seqlen_q)
+ *         bytes, 256-byte aligned (else GQA_ERR_WORKSPACE): a first, small
+ *         kernel writes the work list there (every (sequence, query block)
+ *         ordered by its key-tile count, heaviest first) and the attention
+ *         kernel reads it.  Its previous contents do not matter.
+ *
+ * Two launches on `stream`.  Requirements: dtype == GQA_DTYPE_BF16 and
+ * d == 128 (else GQA_ERR_UNSUPPORTED); 0 <= max_seqlen_q <= total_q
+ * (total_q = 0 or max_seqlen_q = 0 launches nothing and needs no workspace).
+ */
+int gqa_attn_prefill_varlen(const void* q, const void* k, const void* v,
+                            const int* cu_seqlens_q, const int* kv_lens, void* o,
+                            float* lse, int B, int H_q, int H_kv, int d, int total_q,
+                            int max_seqlen_q, int kv_cap, int max_kv_len, int causal,
+                            float scale, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+/* Workspace bytes gqa_attn_prefill_varlen needs; 0 for invalid sizes. */
+size_t gqa_attn_prefill_varlen_workspace_bytes(int B, int H_q, int H_kv, int max_seqlen_q);
 
 #ifdef __cplusplus
 }

@@ -487,6 +487,16 @@ def pin_prefill_varlen(O):
     om, lm = O.decode_multi(q2, k[:2], v[:2], lens2, 0.5)
     _close(o2, np.transpose(om, (0, 2, 1, 3)).reshape(2 * T_q, H_q, d), what="varlen == multi decode")
     _close(l2, np.transpose(lm, (0, 2, 1)).reshape(2 * T_q, H_q), what="varlen lse == multi decode")
+    # A non-causal chunk over an empty cache is the empty result: merged with
+    # a real result it leaves that result unchanged.
+    oe, le = O.prefill_varlen(q[:3], k[:1], v[:1], np.array([0, 3]), np.array([0]), 0.8,
+                              causal=False)
+    assert np.all(oe == 0) and np.all(le == -np.inf)
+    orl, lrl = O.prefill_varlen(q[:3], k[:1], v[:1], np.array([0, 3]), np.array([6]), 0.8,
+                                causal=False)
+    om2, lm2 = O.merge_normalized(oe, le, orl, lrl)
+    _close(om2, orl, what="empty varlen chunk merges as identity")
+    _close(lm2, lrl, what="empty varlen chunk lse")
 
 
 PINS = [

@@ -134,6 +134,54 @@ def test_prefill_rejects_before_launch(kw, status):
     assert _prefill(**kw) == status
 
 
+def _varlen(**kw):
+    a = dict(q=P, k=P, v=P, cu=P2, lens=P2, o=P2, lse=None, B=2, H_q=8, H_kv=2, d=128,
+             total=100, maxq=64, cap=128, maxkv=128, causal=1, scale=0.088, dtype=BF16,
+             ws=ctypes.c_void_p(0x300000), wsb=4096, stream=None)
+    a.update(kw)
+    return binding.lib().gqa_attn_prefill_varlen(
+        a["q"], a["k"], a["v"], a["cu"], a["lens"], a["o"], a["lse"], a["B"], a["H_q"],
+        a["H_kv"], a["d"], a["total"], a["maxq"], a["cap"], a["maxkv"], a["causal"], a["scale"],
+        a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), INVALID),
+    (dict(lens=None), INVALID),
+    (dict(lens=ctypes.c_void_p(0x200002)), INVALID),     # int32 array misaligned
+    (dict(o=ctypes.c_void_p(0x200008)), INVALID),
+    (dict(B=0), INVALID),
+    (dict(total=-1), INVALID),
+    (dict(maxq=101), INVALID),                           # > total_q
+    (dict(maxq=-1), INVALID),
+    (dict(maxkv=0), INVALID),
+    (dict(maxkv=129), INVALID),                          # > kv_cap
+    (dict(H_kv=3), INVALID),
+    (dict(causal=2), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(dtype=F32), UNSUPPORTED),
+    (dict(d=64), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x300010)), WORKSPACE),     # not 256-byte aligned
+    (dict(wsb=255), WORKSPACE),
+    (dict(total=0, maxq=0, ws=None), OK),                # nothing to do: no launch
+    (dict(maxq=0, ws=None), OK),
+])
+def test_prefill_varlen_rejects_before_launch(kw, status):
+    assert _varlen(**kw) == status
+
+
+def test_prefill_varlen_workspace_rule():
+    """One int per (sequence, query block), rounded up to 256 bytes; the
+    query block is 256 rows / gcd(G, 8) heads positions."""
+    L = binding.lib()
+    assert L.gqa_attn_prefill_varlen_workspace_bytes(8, 64, 8, 8192) == 8 * 256 * 4
+    assert L.gqa_attn_prefill_varlen_workspace_bytes(2, 8, 2, 64) == 256        # G=4: 64 rows
+    assert L.gqa_attn_prefill_varlen_workspace_bytes(3, 12, 2, 1000) == 256     # G=6: 128 rows
+    assert L.gqa_attn_prefill_varlen_workspace_bytes(1000, 64, 8, 100) == 16128  # 16000 up
+    assert L.gqa_attn_prefill_varlen_workspace_bytes(0, 64, 8, 100) == 0
+
+
 def test_multi_split_and_workspace_rules():
     L = binding.lib()
     assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 4, 32768, 0, BF16) == 1024
