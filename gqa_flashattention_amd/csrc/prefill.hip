@@ -25,17 +25,18 @@
 //
 // Tiles reach LDS with direct global->LDS loads (no staging registers),
 // XOR-swizzled per 16-byte piece so that both the K operand reads and the
-// V transpose reads are bank-conflict free.  K and V are triple-buffered:
-// step j issues S of tile j+1 and P.V of tile j-1 (32 MFMAs) next to the
-// softmax of tile j, one straight-line block per step.
+// V transpose reads are bank-conflict free.  K and V sit in 4-deep rings:
+// step j issues P.V of tile j-1 and S of tile j+1 (32 MFMAs) with the
+// softmax of tile j spread between them, one straight-line block per step.
 //
 // Softmax in the log2 domain with a lazy per-row reference max: exps use
 // the reference r, p = exp2(s*scale - r); the reference moves only when a
-// tile's max exceeds r + 64 (then r = max - 32, and O and l are rescaled),
-// which in practice happens on the first tile only.  O and l share the
-// reference, so O / l and the LSE are exact.  The common step therefore
-// needs no cross-lane exchange: each lane tests its own 32 scores and a
-// wave vote sends the rare case to a fix-up path that recomputes the tile.
+// tile's max exceeds r + 64 (then r = max - 32, and O and l are rescaled);
+// the prologue sets r from tile 0, so in practice it never moves.  O and
+// l share the reference, so O / l and the LSE are exact.  The common step
+// therefore needs no cross-lane exchange: each lane tests its own 32
+// scores and a wave vote sends the rare case to a fix-up path that
+// recomputes the tile.
 // Row sums are accumulated in fp32 from the unrounded P, so the exported
 // LSE carries no bf16 rounding.
 //
@@ -363,9 +364,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // sequence, each MFMA's LDS operand read three MFMAs ahead, with the
   // softmax of tile j (P = exp2(S*scale - ref), rounded to bf16; fp32 row
   // sums) spread between them so that the matrix unit and the vector ALUs
-  // work at the same time.  Order: P.V key steps 0-1 beside the exps of
-  // S(j) rows 0-31; S(j+1) rows 0-31 (reusing those registers) beside the
-  // exps of rows 32-63; S(j+1) rows 32-63; P.V key steps 2-3.  Returns
+  // work at the same time.  Order: the 16 MFMAs of P.V(j-1), then S(j+1)
+  // rows 0-31 (reusing the registers of S(j) rows 0-31), then rows 32-63.
+  // The 32 exponentials of S(j) are spread evenly over the first 24 slots
+  // (two, one, one per slot): rows 0-31 finish by slot 11 and rows 32-63
+  // by slot 23, just before their registers are overwritten.  Two waves
+  // share a SIMD and run the same sequence in step, so spreading the
+  // exponentials keeps the vector port's load per slot near one MFMA's
+  // duration instead of doubling it for half of the sequence.  Returns
   // this lane's fp32 sum of P(j).
   // `ld` (when not null) lists two tile loads as {kv, buffer, tile}
   // triples; their four instructions are spread over the sequence (one
@@ -376,10 +382,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     constexpr int kb = decltype(kbuf)::value;
     constexpr int vb = decltype(vbuf)::value;
     auto opnd = [&](int i) -> bf16x8 {
-      if (i < 8) return v_opnd(vb, i >> 2, i & 3);
-      if (i < 16) return k_opnd(kb, 0, i - 8);
-      if (i < 24) return k_opnd(kb, 1, i - 16);
-      return v_opnd(vb, 2 + ((i - 24) >> 2), (i - 24) & 3);
+      if (i < 16) return v_opnd(vb, i >> 2, i & 3);
+      if (i < 24) return k_opnd(kb, 0, i - 16);
+      return k_opnd(kb, 1, i - 24);
     };
     float negr = -m_ref;
     // Anchor the softmax inputs here, so that no exponential is hoisted
@@ -387,6 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     asm volatile("" : "+v"(negr));
     float psum = 0.f;
     u32x4 pw[4];
+    float ev[32];   // exponentials of S(j), key order of the lane's scores
     Tile16 Sn;
     constexpr int kAhead = 3;   // operand reads in flight ahead of the MFMA
     bf16x8 ring[kAhead + 1];
@@ -403,27 +409,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       }
       const bf16x8 a = ring[i % (kAhead + 1)];
       const f32x16 zero = {};
-      if (i < 8) {
+      if (i < 16) {
         o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Pprev.p[i >> 2], o[i & 3], 0, 0, 0);
-      } else if (i < 16) {
-        Sn.s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i - 8], i > 8 ? Sn.s[0] : zero,
-                                                          0, 0, 0);
       } else if (i < 24) {
-        Sn.s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i - 16], i > 16 ? Sn.s[1] : zero,
+        Sn.s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i - 16], i > 16 ? Sn.s[0] : zero,
                                                           0, 0, 0);
       } else {
-        const int st = 2 + ((i - 24) >> 2);
-        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Pprev.p[st], o[i & 3], 0, 0, 0);
+        Sn.s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i - 24], i > 24 ? Sn.s[1] : zero,
+                                                          0, 0, 0);
       }
-      if (i < 16) {
-        // Softmax pair q of S(j) rows 32*mt..: keys 32*mt + 8*(q/4) + 4*h2
-        // + 2*(q%4) + {0, 1}.
-        const int mt = i >> 3, q = i & 7;
-        const float e0 = fast_exp2(__builtin_fmaf(T.s[mt][2 * q], sl2, negr));
-        const float e1 = fast_exp2(__builtin_fmaf(T.s[mt][2 * q + 1], sl2, negr));
-        psum += e0 + e1;
-        const unsigned w = pack_bf16x2(e0, e1);
-        // Keep this pair in this slot (not sunk towards its first use).
+      // Exponential k (score k of the lane: rows 32*(k/16).., key 32*(k/16)
+      // + 8*((k%16)/4... as S.s[k/16][k%16]) runs in slot 3k/4.
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        if ((3 * k) / 4 != i) continue;
+        ev[k] = fast_exp2(__builtin_fmaf(T.s[k >> 4][k & 15], sl2, negr));
+        if ((k & 1) == 0) {
+          // Keep this exponential in this slot (not sunk towards its use).
+          asm volatile("" ::"v"(ev[k]));
+          continue;
+        }
+        // Pair k/2 complete: keys 32*mt + 8*(q/4) + 4*h2 + 2*(q%4) + {0, 1}
+        // of S(j) rows 32*mt.., q = (k/2) % 8.
+        const int mt = k >> 4, q = (k >> 1) & 7;
+        psum += ev[k - 1] + ev[k];
+        const unsigned w = pack_bf16x2(ev[k - 1], ev[k]);
         asm volatile("" ::"v"(w), "v"(psum));
         pw[2 * mt + (q >> 2)][q & 3] = w;
         if ((q & 3) == 3) Pcur.p[2 * mt + (q >> 2)] = as_bf16x8(pw[2 * mt + (q >> 2)]);
@@ -452,14 +462,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   for (int st = 0; st < 4; ++st) PB.p[st] = as_bf16x8(u32x4{0, 0, 0, 0});
   compute_s(T, 0);
   __syncthreads();                      // every wave has read K tile 0
+  // The reference starts 32 below the row max of tile 0's visible scores
+  // (every row sees key 0), so the first step does not take the fix-up
+  // path.  The mask is idempotent: step 0 applies it again.
+  if (n_full == 0) mask_tile(T, 0);
+  move_ref(fmaxf(half_max(T.s[0]), half_max(T.s[1])) * sl2);
 
   // Step j: P.V of tile j-1, the softmax of tile j (scores in T) into
   // `pcur`, and S of tile j+1 into T.  Tiles past the wave's last visible
   // one are fully masked (P = 0), so every step runs the same sequence.
   // The softmax uses the current reference; if any weight exceeds 2^64
-  // (some score is more than 64 above the reference: always on the first
-  // tile, rarely later) the lane sum shows it, and the tile's scores are
-  // recomputed from K (still in LDS), the reference moved and P redone.
+  // (some score is more than 64 above the reference: rare once the
+  // prologue has set it from tile 0) the lane sum shows it, and the tile's
+  // scores are recomputed from K (still in LDS), the reference moved and P
+  // redone.
   auto step = [&](auto kbuf, auto vbuf, PTile& pprev, PTile& pcur, int j, const int (*ld)[3]) {
     constexpr int kb = decltype(kbuf)::value;   // K buffer of tile j+1
     if (j >= n_full) mask_tile(T, j);
