@@ -27,6 +27,7 @@ from .attention import (  # noqa: F401
     paged_gather,
     prefill,
     prefill_varlen,
+    prefill_paged,
     prefill_visible_len,
     kv_head_of,
     partial,

@@ -165,8 +165,10 @@ def prefill_varlen(q, k, v, cu_seqlens_q, kv_lens, scale: float, causal: bool = 
     of ADR-0060@5a76ed4 §0.5.1), so with a causal mask its token ``i`` sees
     keys ``j <= kv_lens[b] - S_q_b + i`` -- ``prefill`` with
     ``causal_offset = kv_lens[b] - S_q_b`` (``q_block_meta``, §0.5.3); without
-    one, all ``kv_lens[b]`` keys.  Returns ``(o [total_q, H_q, d],
-    lse [total_q, H_q])``.
+    one, all ``kv_lens[b]`` keys.  A non-causal chunk whose sequence has no
+    cached key at all has no visible key in any row: O = 0 and lse = -inf,
+    the empty result of ``merge_normalized`` (it leaves the other side
+    unchanged).  Returns ``(o [total_q, H_q, d], lse [total_q, H_q])``.
     """
     q = np.asarray(q)
     cu = np.asarray(cu_seqlens_q, dtype=np.int64).reshape(-1)
@@ -181,6 +183,10 @@ def prefill_varlen(q, k, v, cu_seqlens_q, kv_lens, scale: float, causal: bool = 
             continue
         if causal and S_q > L:
             raise ValueError("a causal chunk must be the last S_q of its sequence's positions")
+        if L == 0:
+            o[t0:t1] = 0.0
+            lse[t0:t1] = -np.inf
+            continue
         qb = np.transpose(q[t0:t1], (1, 0, 2))[None]            # [1, H_q, S_q, d]
         ob, lb = prefill(qb, k[b:b + 1], v[b:b + 1], L, scale, causal=causal,
                          causal_offset=L - S_q)
@@ -217,6 +223,16 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, page_size: int, scal
     k = paged_gather(k_pages, block_table, kv_lens, page_size)
     v = paged_gather(v_pages, block_table, kv_lens, page_size)
     return decode_multi(q, k, v, kv_lens, scale)
+
+
+def prefill_paged(q, k_pages, v_pages, block_table, cu_seqlens_q, kv_lens, page_size: int,
+                  scale: float, causal: bool = True):
+    """Varlen prefill (``prefill_varlen``) over a paged K/V cache: the
+    attention is unchanged, only the cache layout differs (``paged_gather``).
+    q: ``[total_q, H_q, d]`` token-packed."""
+    k = paged_gather(k_pages, block_table, kv_lens, page_size)
+    v = paged_gather(v_pages, block_table, kv_lens, page_size)
+    return prefill_varlen(q, k, v, cu_seqlens_q, kv_lens, scale, causal=causal)
 
 
 def prefill_visible_len(rows, S_kv: int, causal: bool, causal_offset: int):

@@ -499,6 +499,36 @@ def pin_prefill_varlen(O):
     _close(lm2, lrl, what="empty varlen chunk lse")
 
 
+
+def pin_prefill_paged(O):
+    """Ragged chunks over a shuffled page pool (scattered here with explicit
+    loops; unused pages and rows NaN) equal the varlen prefill over the
+    contiguous cache they came from, causal and not."""
+    rng = _rng(31)
+    H_q, H_kv, d, page = 4, 2, 4, 4
+    q_lens, lens = (3, 1, 6), (7, 12, 6)
+    B, top = len(lens), max(lens)
+    cu = np.concatenate([[0], np.cumsum(q_lens)])
+    q = rng.standard_normal((int(cu[-1]), H_q, d))
+    k = rng.standard_normal((B, H_kv, top, d))
+    v = rng.standard_normal((B, H_kv, top, d))
+    max_pages = (top + page - 1) // page
+    num_pages = B * max_pages + 2
+    table = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages)
+    kp = np.full((num_pages, H_kv, page, d), np.nan)
+    vp = np.full((num_pages, H_kv, page, d), np.nan)
+    for b in range(B):
+        for j in range(lens[b]):
+            for h in range(H_kv):
+                kp[table[b, j // page], h, j % page] = k[b, h, j]
+                vp[table[b, j // page], h, j % page] = v[b, h, j]
+    for causal in (True, False):
+        o, lse = O.prefill_paged(q, kp, vp, table, cu, np.array(lens), page, 0.7, causal=causal)
+        ro, rl = O.prefill_varlen(q, k, v, cu, np.array(lens), 0.7, causal=causal)
+        _close(o, ro, what=f"paged prefill causal={causal}")
+        _close(lse, rl, what=f"paged prefill lse causal={causal}")
+
+
 PINS = [
     pin_brute_force_decode,
     pin_brute_force_prefill,
@@ -520,4 +550,5 @@ PINS = [
     pin_merge_normalized_chunks,
     pin_paged_gather_round_trip,
     pin_prefill_varlen,
+    pin_prefill_paged,
 ]
