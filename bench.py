@@ -257,7 +257,8 @@ def main():
     multi = wd.kind in ("decode_multi", "decode_paged")
     paged = wd.kind == "decode_paged"
     wp = inputs.WORKLOADS[args.prefill_workload]
-    varlen = wp.kind == "prefill_varlen"
+    varlen = wp.kind in ("prefill_varlen", "prefill_paged")
+    paged_pre = wp.kind == "prefill_paged"
     do_dec = args.only in ("decode", "both")
     do_pre = args.only in ("prefill", "both")
 
@@ -290,11 +291,21 @@ def main():
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         o_dec = torch.empty_like(copies[0]["q"])
     if do_pre:
-        xp = (inputs.make_prefill_varlen if varlen else inputs.make_prefill)(wp, device=dev)
+        if paged_pre:
+            # The contiguous k, v it was scattered from stay for the oracle leg.
+            xp = inputs.make_prefill_paged(wp, wp.page_size, device=dev)
+        else:
+            xp = (inputs.make_prefill_varlen if varlen else inputs.make_prefill)(wp, device=dev)
         o_pre = torch.empty_like(xp["q"])
     torch.cuda.synchronize()
 
     def prefill_call():
+        if paged_pre:
+            gq.prefill_paged(xp["q"], xp["k_pages"], xp["v_pages"], xp["block_table"],
+                             xp["cu_seqlens_q"], xp["kv_lens"], max_seqlen_q=max(wp.q_lens),
+                             max_kv_len=wp.max_kv_len, causal=wp.causal, scale=wp.scale,
+                             out=o_pre, stream=stream)
+            return
         if varlen:
             gq.prefill_varlen(xp["q"], xp["k"], xp["v"], xp["cu_seqlens_q"], xp["kv_lens"],
                               max_seqlen_q=max(wp.q_lens), max_kv_len=wp.max_kv_len,
@@ -385,7 +396,8 @@ def main():
                               "kv_lens": list(wd.lens), "kv_copies": len(copies) if do_dec else 0,
                               "keys_per_split": chunk if do_dec else None},
                    "prefill": ({"B": wp.B, "H_q": wp.H_q, "H_kv": wp.H_kv, "d": wp.d,
-                                "entry_point": "gqa_attn_prefill_varlen",
+                                "entry_point": "gqa_attn_prefill_paged" if paged_pre else
+                                "gqa_attn_prefill_varlen", "page_size": wp.page_size or None,
                                 "q_lens": list(wp.q_lens), "kv_lens": list(wp.lens),
                                 "causal": wp.causal} if varlen else
                                {"B": wp.B, "H_q": wp.H_q, "H_kv": wp.H_kv, "d": wp.d,
@@ -429,7 +441,8 @@ def main():
                           "ms_mean": round(mean(pre_ms), 6), "ms_median": round(median(pre_ms), 6),
                           "flops_per_call": wp.prefill_flops(),
                           "roofline": {"bound": "mfma",
-                                       "kernel": f"prefill_bf16_kernel<{str(varlen).lower()}>",
+                                       "kernel": f"prefill_bf16_kernel<{str(varlen).lower()}, "
+                                                 f"{str(paged_pre).lower()}>",
                                        "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                                        "traffic": traffic_from_profiles("prefill", wp.name),

@@ -41,6 +41,8 @@ SIGNATURES = {
     "gqa_attn_prefill_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                      _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "gqa_attn_prefill_varlen_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "gqa_attn_prefill_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                    _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "gqa_attn_merge": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_longlong, _i, _i, _vp]),
     "gqa_attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                    _i, _i, _f, _i, _i, _vp, _sz, _vp]),
@@ -366,4 +368,43 @@ def prefill_varlen(q, k, v, cu_seqlens_q, kv_lens, max_seqlen_q, max_kv_len=None
                                        workspace.numel() * workspace.element_size(),
                                        _stream(stream))
     _check(st, "gqa_attn_prefill_varlen")
+    return (out, lse) if return_lse else out
+
+
+def prefill_paged(q, k_pages, v_pages, block_table, cu_seqlens_q, kv_lens, max_seqlen_q,
+                  max_kv_len=None, causal=True, scale=None, return_lse=False, out=None, lse=None,
+                  workspace=None, stream=None):
+    """``gqa_attn_prefill_paged`` on torch tensors.
+
+    As :func:`prefill_varlen`, with k_pages/v_pages ``[num_pages,H_kv,page,d]``
+    bf16 and block_table ``[B,max_pages]`` int32 on the device; ``max_kv_len``
+    defaults to ``max_pages * page``.
+    """
+    _require_gpu(q, k_pages, v_pages, block_table, cu_seqlens_q, kv_lens)
+    total_q, H_q, d = q.shape
+    num_pages, H_kv, page, _ = k_pages.shape
+    B, max_pages = block_table.shape
+    for t in (block_table, cu_seqlens_q, kv_lens):
+        if t.dtype != torch.int32:
+            raise TypeError("block_table, cu_seqlens_q and kv_lens must be int32")
+    if cu_seqlens_q.numel() != B + 1 or kv_lens.numel() != B:
+        raise ValueError("cu_seqlens_q must hold B+1 entries and kv_lens B")
+    max_kv_len = max_pages * page if max_kv_len is None else int(max_kv_len)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((total_q, H_q), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = prefill_varlen_workspace_bytes(B, H_q, H_kv, int(max_seqlen_q))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib().gqa_attn_prefill_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                      _ptr(cu_seqlens_q), _ptr(kv_lens), _ptr(out),
+                                      _ptr(lse) if return_lse else None, B, H_q, H_kv, d, total_q,
+                                      int(max_seqlen_q), page, max_pages, num_pages, max_kv_len,
+                                      int(bool(causal)), scale, dt, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream))
+    _check(st, "gqa_attn_prefill_paged")
     return (out, lse) if return_lse else out

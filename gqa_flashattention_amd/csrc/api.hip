@@ -525,11 +525,14 @@ size_t gqa_attn_prefill_varlen_workspace_bytes(int B, int H_q, int H_kv, int max
   return gqa::prefill_varlen_sched_bytes(B, n_qblk);
 }
 
-int gqa_attn_prefill_varlen(const void* q, const void* k, const void* v, const int* cu_seqlens_q,
-                            const int* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
-                            int d, int total_q, int max_seqlen_q, int kv_cap, int max_kv_len,
-                            int causal, float scale, int dtype, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+// Varlen prefill on a contiguous cache (block_table null) or a paged one.
+static int prefill_varlen_common(const void* q, const void* k, const void* v,
+                                 const int* cu_seqlens_q, const int* kv_lens, void* o, float* lse,
+                                 int B, int H_q, int H_kv, int d, int total_q, int max_seqlen_q,
+                                 int kv_cap, int max_kv_len, int causal, float scale, int dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 const int* block_table, int page_shift, int max_pages,
+                                 int num_pages) {
   if (!q || !k || !v || !o || !cu_seqlens_q || !kv_lens) return GQA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GQA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(cu_seqlens_q) |
@@ -576,8 +579,46 @@ int gqa_attn_prefill_varlen(const void* q, const void* k, const void* v, const i
   p.cu_seqlens_q = cu_seqlens_q;
   p.kv_lens = kv_lens;
   p.sched = static_cast<int*>(workspace);
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.page_shift = page_shift;
+  p.num_pages = num_pages;
   hipError_t e = gqa::launch_prefill(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int gqa_attn_prefill_varlen(const void* q, const void* k, const void* v, const int* cu_seqlens_q,
+                            const int* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
+                            int d, int total_q, int max_seqlen_q, int kv_cap, int max_kv_len,
+                            int causal, float scale, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return prefill_varlen_common(q, k, v, cu_seqlens_q, kv_lens, o, lse, B, H_q, H_kv, d, total_q,
+                               max_seqlen_q, kv_cap, max_kv_len, causal, scale, dtype, workspace,
+                               workspace_bytes, stream, nullptr, 0, 0, 0);
+}
+
+int gqa_attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
+                           const int* block_table, const int* cu_seqlens_q, const int* kv_lens,
+                           void* o, float* lse, int B, int H_q, int H_kv, int d, int total_q,
+                           int max_seqlen_q, int page_size, int max_pages_per_seq, int num_pages,
+                           int max_kv_len, int causal, float scale, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!block_table || (reinterpret_cast<uintptr_t>(block_table) & 3u)) return GQA_ERR_INVALID_ARG;
+  const int sh = page_shift_of(page_size);
+  if (sh < 0 || max_pages_per_seq < 1 || num_pages < 1) return GQA_ERR_INVALID_ARG;
+  if (H_kv >= 1 && (long long)num_pages * H_kv * page_size * kD >= (1LL << 62))
+    return GQA_ERR_INVALID_ARG;
+  const long long cap = (long long)max_pages_per_seq * page_size;
+  if (max_kv_len < 1 || max_kv_len > cap) return GQA_ERR_INVALID_ARG;
+  if ((long long)B * max_pages_per_seq >= (1LL << 31)) return GQA_ERR_INVALID_ARG;
+  // The kernel stages one table row in LDS: at most kPrefillMaxPages pages
+  // of a sequence are reachable.
+  if (((long long)max_kv_len + page_size - 1) / page_size > gqa::kPrefillMaxPages)
+    return GQA_ERR_UNSUPPORTED;
+  return prefill_varlen_common(q, k_pages, v_pages, cu_seqlens_q, kv_lens, o, lse, B, H_q, H_kv,
+                               d, total_q, max_seqlen_q, (int)(cap < 0x7fffffff ? cap : 0x7fffffff),
+                               max_kv_len, causal, scale, dtype, workspace, workspace_bytes,
+                               stream, block_table, sh, max_pages_per_seq, num_pages);
 }
 
 }  // extern "C"

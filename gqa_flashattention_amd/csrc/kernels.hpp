@@ -52,7 +52,17 @@ struct PrefillParams {
   const int* cu_seqlens_q;
   const int* kv_lens;
   int* sched;
+  // Paged cache (varlen only; block_table null otherwise): k, v are
+  // [num_pages, H_kv, 1 << page_shift, d] pools; position j of sequence b is
+  // row j % page of physical page block_table[b * max_pages + j / page].
+  const int* block_table;
+  int max_pages;
+  int page_shift;
+  int num_pages;        // pool size; table entries are clamped into [0, num_pages)
 };
+
+// Longest block-table row the paged prefill kernel stages in LDS.
+constexpr int kPrefillMaxPages = 8192;
 
 struct MergeParams {
   const void* o_a;      // [rows, d]

@@ -95,9 +95,14 @@ using Int = std::integral_constant<int, N>;
 // b's chunk is q/o rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of
 // [total_q, H_q, d] (lse [total_q, H_q]) against kv_lens[b] cached keys,
 // with causal offset kv_lens[b] - S_q_b; otherwise q/o are [B, H_q, S_q, d].
-template <bool kVarlen>
+// kPaged (with kVarlen): K/V come from page pools through the block table.
+template <bool kVarlen, bool kPaged>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
+  static_assert(kVarlen || !kPaged, "the paged form is a varlen batch");
   __shared__ __attribute__((aligned(1024))) __bf16 sK[kBufs][kTileElems];
+  // Paged form: this sequence's block-table row, clamped into the pool
+  // (the 32 KiB the tile rings leave free).
+  __shared__ int sPage[kPaged ? kPrefillMaxPages : 1];
   __shared__ __attribute__((aligned(1024))) __bf16 sV[kBufs][kTileElems];
 
   // Workgroup -> (position block, sequence, head group, KV head).
@@ -183,8 +188,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   }
   n_full = min(n_full, n_live);
 
-  const __bf16* Kg = static_cast<const __bf16*>(p.k) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
-  const __bf16* Vg = static_cast<const __bf16*>(p.v) + ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
+  // K/V of this (sequence, KV head); the paged form addresses the pools.
+  const size_t kv_base = kPaged ? 0 : ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
+  const __bf16* Kg = static_cast<const __bf16*>(p.k) + kv_base;
+  const __bf16* Vg = static_cast<const __bf16*>(p.v) + kv_base;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   // Q^T operand (B of S^T): query qrow, d = 16*ks + 8*h2 .. +8.  A negative
   // scale is applied exactly by flipping Q's sign bits.
@@ -245,6 +253,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // rows is touched); those keys are masked and their zero V rows get
   // weight 0.  Tile indices past the last tile are clamped to it (the
   // buffers they fill are never read).
+  // Paged form: a wave's two instructions cover rows 8w .. 8w+7 of the
+  // tile, which lie in one page (pages hold at least 16 rows, a power of
+  // two).  The resource is based so that those rows' offsets within the
+  // tile land on them in the page, and it ends at the sequence's last key.
   constexpr int kInsts = kBN / 4 / kWaves;   // 1 KiB (4-row) loads per wave
   int ld_off[2][kInsts];                     // [K, V][instruction]: byte offset in a tile
 #pragma unroll
@@ -258,16 +270,40 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // into LDS buffer `buf`.  Issued as inline assembly: the compiler would
   // otherwise make the next LDS read wait for it (it cannot tell the
   // addresses apart).  All loads are waited for before each barrier.
-  auto tile_load_part = [&](int kv, int buf, int tile, int i) {
+  // Physical page of this wave's rows of tile `tile` (paged form).
+  auto page_of = [&](int tile) -> int {
+    if constexpr (kPaged) {
+      tile = min(tile, ntiles - 1);
+      // Staged entries: 0 .. min(last page of the tiles, max_pages, limit).
+      const int lp = min((tile * kBN + 8 * wv) >> p.page_shift,
+                         min(p.max_pages, kPrefillMaxPages) - 1);
+      return __builtin_amdgcn_readfirstlane(sPage[lp]);
+    } else {
+      return 0;
+    }
+  };
+  auto tile_load_part = [&](int kv, int buf, int tile, int i, int pg) {
     tile = min(tile, ntiles - 1);
-    const u32x4 rsrc = buffer_rsrc((kv ? Vg : Kg) + (size_t)tile * (kBN * kD),
-                                   (unsigned)(S_kv - tile * kBN) * (kD * 2));
+    u32x4 rsrc;
+    if constexpr (kPaged) {
+      const int row0 = tile * kBN + 8 * wv;
+      const int valid = min(max(S_kv - row0, 0), 8);
+      const size_t e = ((size_t)pg * p.H_kv + kvh) * ((size_t)kD << p.page_shift) +
+                       (size_t)(row0 & ((1 << p.page_shift) - 1)) * kD;
+      const uintptr_t a = reinterpret_cast<uintptr_t>((kv ? Vg : Kg) + e) -
+                          (uintptr_t)(8 * wv) * (kD * 2);
+      rsrc = buffer_rsrc(reinterpret_cast<const void*>(a), (unsigned)(8 * wv + valid) * (kD * 2));
+    } else {
+      rsrc = buffer_rsrc((kv ? Vg : Kg) + (size_t)tile * (kBN * kD),
+                         (unsigned)(S_kv - tile * kBN) * (kD * 2));
+    }
     dma_load_x4(ld_off[kv][i], rsrc,
                 (kv ? lds_v0 : lds_k0) + buf * kTileBytes + 4 * (kInsts * wave + i) * kD * 2);
   };
   auto tile_load = [&](int kv, int buf, int tile) {
+    const int pg = page_of(tile);
 #pragma unroll
-    for (int i = 0; i < kInsts; ++i) tile_load_part(kv, buf, tile, i);
+    for (int i = 0; i < kInsts; ++i) tile_load_part(kv, buf, tile, i, pg);
   };
 
   // S^T of one tile from K buffer `kb`.
@@ -373,12 +409,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // exponentials keeps the vector port's load per slot near one MFMA's
   // duration instead of doubling it for half of the sequence.  Returns
   // this lane's fp32 sum of P(j).
-  // `ld` (when not null) lists two tile loads as {kv, buffer, tile}
-  // triples; their four instructions are spread over the sequence (one
+  // `ld` (when not null) lists two tile loads as {kv, buffer, tile, page}
+  // entries; their four instructions are spread over the sequence (one
   // every eighth MFMA) so that the load path is fed gradually instead of
   // stalling the waves at the start of the group.
   auto mma_step = [&](auto kbuf, auto vbuf, Tile16& T, const PTile& Pprev, PTile& Pcur,
-                      const int (*ld)[3]) {
+                      const int (*ld)[4]) {
     constexpr int kb = decltype(kbuf)::value;
     constexpr int vb = decltype(vbuf)::value;
     auto opnd = [&](int i) -> bf16x8 {
@@ -405,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       if (i + kAhead < 32) ring[(i + kAhead) % (kAhead + 1)] = opnd(i + kAhead);
       if (ld != nullptr && (i & 7) == 2) {
         const int* l = ld[i >> 4];
-        tile_load_part(l[0], l[1], l[2], (i >> 3) & 1);
+        tile_load_part(l[0], l[1], l[2], (i >> 3) & 1, l[3]);
       }
       const bf16x8 a = ring[i % (kAhead + 1)];
       const f32x16 zero = {};
@@ -445,7 +481,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   };
 
   // Prologue: K tiles 0-2 and V tile 0 in LDS, V buffer 3 (read as tile
-  // -1 by the first step, with P = 0) zeroed; S of tile 0.
+  // -1 by the first step, with P = 0) zeroed; S of tile 0.  The paged
+  // form first stages the block-table entries of the pages its tiles touch.
+  if constexpr (kPaged) {
+    const int n_lp = min(min(((ntiles * kBN - 1) >> p.page_shift) + 1, p.max_pages),
+                         kPrefillMaxPages);
+    const int* trow = p.block_table + (size_t)b * p.max_pages;
+    for (int i = t; i < n_lp; i += kThreads) sPage[i] = min(max(trow[i], 0), p.num_pages - 1);
+    __syncthreads();
+  }
   tile_load(0, 0, 0);
   if (ntiles > 1) tile_load(0, 1, 1);
   if (ntiles > 2) tile_load(0, 2, 2);
@@ -476,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // prologue has set it from tile 0) the lane sum shows it, and the tile's
   // scores are recomputed from K (still in LDS), the reference moved and P
   // redone.
-  auto step = [&](auto kbuf, auto vbuf, PTile& pprev, PTile& pcur, int j, const int (*ld)[3]) {
+  auto step = [&](auto kbuf, auto vbuf, PTile& pprev, PTile& pcur, int j, const int (*ld)[4]) {
     constexpr int kb = decltype(kbuf)::value;   // K buffer of tile j+1
     if (j >= n_full) mask_tile(T, j);
     float psum = mma_step(kbuf, vbuf, T, pprev, pcur, ld);
@@ -497,8 +541,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // barrier at the end.
   auto group = [&](auto gsel, int j) {
     constexpr int G = decltype(gsel)::value;
-    const int ldv[2][3] = {{1, (2 * G + 1) % 4, j + 1}, {1, (2 * G + 2) % 4, j + 2}};
-    const int ldk[2][3] = {{0, (2 * G + 3) % 4, j + 3}, {0, (2 * G + 4) % 4, j + 4}};
+    const int ldv[2][4] = {{1, (2 * G + 1) % 4, j + 1, page_of(j + 1)},
+                           {1, (2 * G + 2) % 4, j + 2, page_of(j + 2)}};
+    const int ldk[2][4] = {{0, (2 * G + 3) % 4, j + 3, page_of(j + 3)},
+                           {0, (2 * G + 4) % 4, j + 4, page_of(j + 4)}};
     step(Int<(2 * G + 1) % 4>(), Int<(2 * G + 3) % 4>(), PB, PA, j, ldv);
     if (j + 1 < ntiles) {
       step(Int<(2 * G + 2) % 4>(), Int<(2 * G) % 4>(), PA, PB, j + 1, ldk);
@@ -628,11 +674,16 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
                        p.sched, shift);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3((unsigned)nwg), dim3(kThreads), 0, stream,
-                       p);
+    if (p.block_table != nullptr) {
+      hipLaunchKernelGGL((prefill_bf16_kernel<true, true>), dim3((unsigned)nwg), dim3(kThreads), 0,
+                         stream, p);
+    } else {
+      hipLaunchKernelGGL((prefill_bf16_kernel<true, false>), dim3((unsigned)nwg), dim3(kThreads),
+                         0, stream, p);
+    }
   } else {
-    hipLaunchKernelGGL(prefill_bf16_kernel<false>, dim3((unsigned)nwg), dim3(kThreads), 0, stream,
-                       p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<false, false>), dim3((unsigned)nwg), dim3(kThreads), 0,
+                       stream, p);
   }
   return hipGetLastError();
 }

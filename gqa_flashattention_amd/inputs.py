@@ -62,7 +62,7 @@ class Workload:
 
     @property
     def max_kv_len(self) -> int:
-        if self.kind.startswith("decode") or self.kind == "prefill_varlen":
+        if self.kind.startswith("decode") or self.kind in ("prefill_varlen", "prefill_paged"):
             return max(self.lens)
         return self.S_kv
 
@@ -91,7 +91,7 @@ class Workload:
 
     def prefill_flops(self) -> int:
         """Algorithmic FLOPs: 2*d for Q.K^T plus 2*d for P.V per visible pair."""
-        if self.kind == "prefill_varlen":
+        if self.kind in ("prefill_varlen", "prefill_paged"):
             return 4 * self.d * self.H_q * self.varlen_visible_pairs()
         return 4 * self.d * self.B * self.H_q * self.visible_pairs_per_head()
 
@@ -150,6 +150,14 @@ WORKLOADS = {
                                            lens=(8192, 12288, 32768, 2048, 65536, 4096, 300,
                                                  16384),
                                            kv_cap=65536, causal=True),
+    # The same batch with its caches in a pool of 16-position pages placed
+    # in a seeded random order.
+    "prefill_paged_llama70b_b8_p16": Workload("prefill_paged_llama70b_b8_p16", "prefill_paged",
+                                              B=8, H_q=64, H_kv=8, d=128, dtype="bf16",
+                                              q_lens=(8192, 4096, 2048, 1024, 512, 256, 37, 1),
+                                              lens=(8192, 12288, 32768, 2048, 65536, 4096, 300,
+                                                    16384),
+                                              kv_cap=65536, causal=True, page_size=16),
 }
 
 # Seed per workload: 20260000 + its position in the list above (1-based).
@@ -209,6 +217,18 @@ def make_decode_paged(w: Workload, page_size: int, device="cpu", seed=None, spar
     """
     x = make_decode_multi(w, device=device, seed=seed)
     seed = SEEDS.get(w.name, 1) if seed is None else seed
+    k_pages, v_pages, table = scatter_pages(w, x["k"], x["v"], page_size, seed, spare_pages, device)
+    return {"q": x["q"], "k_pages": k_pages, "v_pages": v_pages,
+            "block_table": table, "kv_lens": x["kv_lens"], "k": x["k"], "v": x["v"]}
+
+
+def scatter_pages(w: Workload, k, v, page_size: int, seed: int, spare_pages: int, device):
+    """Contiguous caches ``[B,H_kv,kv_cap,d]`` scattered into a pool of pages
+    ``[num_pages,H_kv,page_size,d]``: each sequence's logical pages take
+    physical pages in a seeded random order (generator ``seed*16 + 4``),
+    ``spare_pages`` extra pages are NaN, table entries past a sequence's
+    pages name a NaN page, and rows of a last page past the length are NaN.
+    Returns the K and V pools and the block table ``[B, max_pages]`` int32."""
     max_pages = (w.kv_cap + page_size - 1) // page_size
     need = [(L + page_size - 1) // page_size for L in w.lens]
     num_pages = sum(need) + spare_pages
@@ -226,10 +246,21 @@ def make_decode_paged(w: Workload, page_size: int, device="cpu", seed=None, spar
             nxt += 1
             table[b, lp] = pp
             rows = min(page_size, L - lp * page_size)
-            k_pages[pp, :, :rows] = x["k"][b, :, lp * page_size:lp * page_size + rows]
-            v_pages[pp, :, :rows] = x["v"][b, :, lp * page_size:lp * page_size + rows]
-    return {"q": x["q"], "k_pages": k_pages, "v_pages": v_pages,
-            "block_table": table.to(device), "kv_lens": x["kv_lens"], "k": x["k"], "v": x["v"]}
+            k_pages[pp, :, :rows] = k[b, :, lp * page_size:lp * page_size + rows]
+            v_pages[pp, :, :rows] = v[b, :, lp * page_size:lp * page_size + rows]
+    return k_pages, v_pages, table.to(device)
+
+
+def make_prefill_paged(w: Workload, page_size: int, device="cpu", seed=None, spare_pages=3):
+    """Paged-cache varlen prefill inputs: the inputs of ``make_prefill_varlen``
+    (same seeds, so the same values) with K/V scattered as by
+    ``scatter_pages``.  Returns q, k_pages, v_pages, block_table,
+    cu_seqlens_q, kv_lens and the contiguous k, v."""
+    x = make_prefill_varlen(w, device=device, seed=seed)
+    seed = SEEDS.get(w.name, 1) if seed is None else seed
+    k_pages, v_pages, table = scatter_pages(w, x["k"], x["v"], page_size, seed, spare_pages, device)
+    x.update({"k_pages": k_pages, "v_pages": v_pages, "block_table": table})
+    return x
 
 
 def make_prefill(w: Workload, device="cpu", seed=None, nan_pad=True, kv_cap=None):

@@ -14,6 +14,8 @@
  *                     a batch of prefill chunks of different lengths
  *                     (token-packed), each the newest positions of its
  *                     sequence's cache.
+ *   gqa_attn_prefill_paged
+ *                     the same over a paged K/V cache (block table).
  *   gqa_attn_merge    stitches two (O, lse) results over disjoint key sets.
  *   gqa_attn_decode_paged
  *                     decode (T_q >= 1) over a paged K/V cache (block table).
@@ -395,6 +397,36 @@ int gqa_attn_prefill_varlen(const void* q, const void* k, const void* v,
                             size_t workspace_bytes, void* stream);
 /* Workspace bytes gqa_attn_prefill_varlen needs; 0 for invalid sizes. */
 size_t gqa_attn_prefill_varlen_workspace_bytes(int B, int H_q, int H_kv, int max_seqlen_q);
+
+/*
+ * Varlen prefill over a paged K/V cache: gqa_attn_prefill_varlen with the
+ * cache in a page pool addressed through a block table (the driver-chosen
+ * placement of each KV block, §2.1, made explicit).  Same q, o, lse,
+ * cu_seqlens_q, kv_lens, causal, max_seqlen_q, scale and workspace (its
+ * size from gqa_attn_prefill_varlen_workspace_bytes) as there.
+ *
+ *   k_pages, v_pages  [num_pages, H_kv, page_size, d] bf16 pools, read-only:
+ *         position j of sequence b is row j % page_size of physical page
+ *         block_table[b * max_pages_per_seq + j / page_size]
+ *   block_table  [B, max_pages_per_seq] int32 DEVICE array, 4-byte aligned.
+ *         Entries outside [0, num_pages) are clamped into the pool (wrong
+ *         values, never an access outside it); entries past a sequence's
+ *         pages are not read.
+ *   page_size    a power of two, 16 .. 65536
+ *   max_kv_len   an upper bound of every kv_lens[b] (clamped to it),
+ *         1 <= max_kv_len <= max_pages_per_seq * page_size
+ *
+ * Requirements as for gqa_attn_prefill_varlen, and at most 8192 pages per
+ * sequence (ceil(max_kv_len / page_size) <= 8192, else GQA_ERR_UNSUPPORTED:
+ * the kernel stages a sequence's table row in LDS).
+ */
+int gqa_attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
+                           const int* block_table, const int* cu_seqlens_q,
+                           const int* kv_lens, void* o, float* lse, int B, int H_q,
+                           int H_kv, int d, int total_q, int max_seqlen_q, int page_size,
+                           int max_pages_per_seq, int num_pages, int max_kv_len,
+                           int causal, float scale, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

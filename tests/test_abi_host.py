@@ -171,6 +171,39 @@ def test_prefill_varlen_rejects_before_launch(kw, status):
     assert _varlen(**kw) == status
 
 
+def _paged_prefill(**kw):
+    a = dict(q=P, k=P, v=P, table=P2, cu=P2, lens=P2, o=P2, lse=None, B=2, H_q=8, H_kv=2, d=128,
+             total=100, maxq=64, page=16, max_pages=8, num_pages=20, maxkv=128, causal=1,
+             scale=0.088, dtype=BF16, ws=ctypes.c_void_p(0x300000), wsb=4096, stream=None)
+    a.update(kw)
+    return binding.lib().gqa_attn_prefill_paged(
+        a["q"], a["k"], a["v"], a["table"], a["cu"], a["lens"], a["o"], a["lse"], a["B"],
+        a["H_q"], a["H_kv"], a["d"], a["total"], a["maxq"], a["page"], a["max_pages"],
+        a["num_pages"], a["maxkv"], a["causal"], a["scale"], a["dtype"], a["ws"], a["wsb"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(table=None), INVALID),
+    (dict(table=ctypes.c_void_p(0x200002)), INVALID),
+    (dict(page=24), INVALID),                            # not a power of two
+    (dict(page=8), INVALID),                             # below 16
+    (dict(max_pages=0), INVALID),
+    (dict(num_pages=0), INVALID),
+    (dict(maxkv=129), INVALID),                          # > max_pages * page
+    (dict(maxkv=0), INVALID),
+    (dict(cu=None), INVALID),
+    (dict(maxq=101), INVALID),
+    (dict(H_kv=3), INVALID),
+    (dict(dtype=F32), UNSUPPORTED),
+    (dict(page=16, max_pages=9000, maxkv=16 * 8193), UNSUPPORTED),   # 8193 pages of a sequence
+    (dict(ws=None), WORKSPACE),
+    (dict(maxq=0, ws=None), OK),
+])
+def test_prefill_paged_rejects_before_launch(kw, status):
+    assert _paged_prefill(**kw) == status
+
+
 def test_prefill_varlen_workspace_rule():
     """One int per (sequence, query block), rounded up to 256 bytes; the
     query block is 256 rows / gcd(G, 8) heads positions."""
