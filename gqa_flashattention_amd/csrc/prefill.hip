@@ -588,12 +588,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
 // Tile count of a varlen work item (b, pblk): the key tiles its workgroup
 // walks (0 past the chunk's end).  Mirrors the extent computed in the
 // attention kernel.
-__device__ __forceinline__ int varlen_item_cost(const PrefillParams& p, int item) {
+// `cu` and `lens` are the length arrays, in LDS or in global memory.
+__device__ __forceinline__ int varlen_item_cost(const PrefillParams& p, const int* cu,
+                                                const int* lens, int item) {
   const int b = item / p.n_qblk, pblk = item % p.n_qblk;
-  const int t0 = min(max(p.cu_seqlens_q[b], 0), p.S_q);
-  const int t1 = min(max(p.cu_seqlens_q[b + 1], t0), p.S_q);
+  const int t0 = min(max(cu[b], 0), p.S_q);
+  const int t1 = min(max(cu[b + 1], t0), p.S_q);
   const int S_q = t1 - t0;
-  const int S_kv = min(max(p.kv_lens[b], 0), p.S_kv);
+  const int S_kv = min(max(lens[b], 0), p.S_kv);
   const int rows = 32 * (kWaves / p.heads_per_wg);
   const int P0 = pblk * rows;
   if (P0 >= S_q) return 0;
@@ -604,6 +606,7 @@ __device__ __forceinline__ int varlen_item_cost(const PrefillParams& p, int item
 
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBins = 2048;
+constexpr int kSchedStagedB = 4096;   // batches up to this size read their lengths from LDS
 
 // The varlen work list: every item b * n_qblk + pblk, ordered by tile count
 // (bins of 2^shift tiles), heaviest first.  One workgroup: histogram of the
@@ -615,11 +618,23 @@ __global__ __launch_bounds__(kSchedThreads) void prefill_varlen_schedule_kernel(
                                                                                int shift) {
   __shared__ int hist[kSchedBins];
   __shared__ int scan[kSchedThreads];
+  __shared__ int s_cu[kSchedStagedB + 1], s_len[kSchedStagedB];
   const int t = threadIdx.x;
   const int n = p.B * p.n_qblk;
+  // One round of global loads: the lengths of up to kSchedStagedB
+  // sequences go to LDS, and both passes below read them there.
+  const bool staged = p.B <= kSchedStagedB;
+  if (staged) {
+    for (int i = t; i <= p.B; i += kSchedThreads) s_cu[i] = p.cu_seqlens_q[i];
+    for (int i = t; i < p.B; i += kSchedThreads) s_len[i] = p.kv_lens[i];
+  }
+  const int* cu = staged ? s_cu : p.cu_seqlens_q;
+  const int* lens = staged ? s_len : p.kv_lens;
   for (int i = t; i < kSchedBins; i += kSchedThreads) hist[i] = 0;
   __syncthreads();
-  auto bin_of = [&](int item) { return min(varlen_item_cost(p, item) >> shift, kSchedBins - 1); };
+  auto bin_of = [&](int item) {
+    return min(varlen_item_cost(p, cu, lens, item) >> shift, kSchedBins - 1);
+  };
   for (int i = t; i < n; i += kSchedThreads) atomicAdd(&hist[bin_of(i)], 1);
   __syncthreads();
   // Descending order: thread t owns bins NB-1-2t and NB-2-2t.

@@ -223,3 +223,24 @@ def test_prefill_varlen_work_list_is_sorted_permutation():
     assert tiles[0] == -(-20000 // 64)      # the 512-token chunk over 20000 keys leads
     assert tiles[-1] == 0                   # blocks past a chunk's end come last
     _check_all(x, w, o, lse, "work list batch")
+
+
+def test_prefill_varlen_work_list_large_batch():
+    """More sequences than the pre-pass stages in LDS (4100 > 4096): it reads
+    the lengths from global memory instead; the list is still a sorted
+    permutation and every chunk matches the oracle."""
+    B = 4100
+    g = torch.Generator().manual_seed(3800)
+    lens = (torch.randint(1, 41, (B,), generator=g)).tolist()
+    q_lens = [min(L, int(x)) for L, x in zip(lens, torch.randint(0, 3, (B,), generator=g))]
+    w = _workload(8, 1, q_lens, lens, 40)
+    banner("prefill_varlen_work_list_large_batch", B)
+    x = inputs.make_prefill_varlen(w, device=DEV, seed=3800)
+    need = gq.prefill_varlen_workspace_bytes(B, 8, 1, max(q_lens))
+    ws = torch.full((need,), 0x55, dtype=torch.uint8, device=DEV)
+    o, lse = _run(x, w, workspace=ws)
+    lst = ws[:4 * B].view(torch.int32).cpu().tolist()     # one 32-position block per sequence
+    assert sorted(lst) == list(range(B))
+    tiles = [_item_tiles(w, i, 1, 32) for i in lst]
+    assert all(a >= b for a, b in zip(tiles, tiles[1:]))
+    _check_all(x, w, o, lse, "large batch")
