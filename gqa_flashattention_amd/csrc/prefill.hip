@@ -604,67 +604,98 @@ __device__ __forceinline__ int varlen_item_cost(const PrefillParams& p, const in
   return (kend + kBN - 1) / kBN;
 }
 
-constexpr int kSchedThreads = 1024;
+constexpr int kSchedThreads = 256;
 constexpr int kSchedBins = 2048;
+constexpr int kSchedPer = kSchedBins / kSchedThreads;   // bins per thread in the scan
 constexpr int kSchedStagedB = 4096;   // batches up to this size read their lengths from LDS
 
 // The varlen work list: every item b * n_qblk + pblk, ordered by tile count
-// (bins of 2^shift tiles), heaviest first.  One workgroup: histogram of the
-// bins in LDS, a descending exclusive scan, then each item placed at its
-// bin's cursor.  Items within a bin land in any order; the result of each
-// item does not depend on when it runs.
-__global__ __launch_bounds__(kSchedThreads) void prefill_varlen_schedule_kernel(PrefillParams p,
-                                                                               int* list,
-                                                                               int shift) {
-  __shared__ int hist[kSchedBins];
-  __shared__ int scan[kSchedThreads];
-  __shared__ int s_cu[kSchedStagedB + 1], s_len[kSchedStagedB];
+// (bins of 2^shift tiles), heaviest first.  One workgroup of 4 waves: the
+// lengths staged in LDS (batches of up to kSchedStagedB sequences; larger
+// ones read them from global memory), a histogram of the bins in LDS, a
+// descending exclusive scan (each thread sums 8 bins, a shuffle scan within
+// each wave, then the wave totals), and each item placed at its bin's
+// cursor.  Items within a bin land in any order; the result of each item
+// does not depend on when it runs.
+template <bool kStaged>
+__device__ __forceinline__ void varlen_schedule(const PrefillParams& p, int* list, int shift,
+                                                int* hist, int* wsum, const int* cu,
+                                                const int* lens) {
   const int t = threadIdx.x;
   const int n = p.B * p.n_qblk;
-  // One round of global loads: the lengths of up to kSchedStagedB
-  // sequences go to LDS, and both passes below read them there.
-  const bool staged = p.B <= kSchedStagedB;
-  if (staged) {
-    for (int i = t; i <= p.B; i += kSchedThreads) s_cu[i] = p.cu_seqlens_q[i];
-    for (int i = t; i < p.B; i += kSchedThreads) s_len[i] = p.kv_lens[i];
-  }
-  const int* cu = staged ? s_cu : p.cu_seqlens_q;
-  const int* lens = staged ? s_len : p.kv_lens;
-  for (int i = t; i < kSchedBins; i += kSchedThreads) hist[i] = 0;
-  __syncthreads();
   auto bin_of = [&](int item) {
     return min(varlen_item_cost(p, cu, lens, item) >> shift, kSchedBins - 1);
   };
-  for (int i = t; i < n; i += kSchedThreads) atomicAdd(&hist[bin_of(i)], 1);
+  const int lane = t & 63, wave = t >> 6;
+  // Most items of a ragged batch lie past their chunk's end (bin 0): that
+  // bin is counted and filled one wave at a time (a ballot and one atomic),
+  // so its items do not serialise on one LDS address.
+  for (int i0 = 0; i0 < n; i0 += kSchedThreads) {
+    const int i = i0 + t;
+    const int bin = i < n ? bin_of(i) : -1;
+    const unsigned long long zero = __ballot(bin == 0);
+    if (bin > 0) atomicAdd(&hist[bin], 1);
+    if (lane == 0 && zero != 0) atomicAdd(&hist[0], __popcll(zero));
+  }
   __syncthreads();
-  // Descending order: thread t owns bins NB-1-2t and NB-2-2t.
-  constexpr int kPer = kSchedBins / kSchedThreads;
-  int local[kPer], sum = 0;
+  // Descending order: thread t owns bins NB-1-8t .. NB-8-8t.
+  int local[kSchedPer], sum = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    local[j] = hist[kSchedBins - 1 - (kPer * t + j)];
+  for (int j = 0; j < kSchedPer; ++j) {
+    local[j] = hist[kSchedBins - 1 - (kSchedPer * t + j)];
     sum += local[j];
   }
-  scan[t] = sum;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {   // inclusive Hillis-Steele scan
-    const int v = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += v;
-    __syncthreads();
-  }
-  int base = scan[t] - sum;   // exclusive prefix of thread t's first bin
+  int incl = sum;   // inclusive scan of the thread sums within the wave
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    hist[kSchedBins - 1 - (kPer * t + j)] = base;   // becomes the bin's cursor
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = incl - sum;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+#pragma unroll
+  for (int j = 0; j < kSchedPer; ++j) {
+    hist[kSchedBins - 1 - (kSchedPer * t + j)] = base;   // becomes the bin's cursor
     base += local[j];
   }
   __syncthreads();
   // Both passes bin each item alike (the length arrays are read-only
   // meanwhile), so every position is below n; the bound only guards the list.
-  for (int i = t; i < n; i += kSchedThreads) {
-    const int pos = atomicAdd(&hist[bin_of(i)], 1);
+  for (int i0 = 0; i0 < n; i0 += kSchedThreads) {
+    const int i = i0 + t;
+    const int bin = i < n ? bin_of(i) : -1;
+    const unsigned long long zero = __ballot(bin == 0);
+    int zbase = 0;
+    if (lane == 0 && zero != 0) zbase = atomicAdd(&hist[0], __popcll(zero));
+    zbase = __shfl(zbase, 0, 64);
+    int pos = n;
+    if (bin == 0) {
+      pos = zbase + __popcll(zero & ((1ull << lane) - 1ull));
+    } else if (bin > 0) {
+      pos = atomicAdd(&hist[bin], 1);
+    }
     if (pos < n) list[pos] = i;
+  }
+}
+
+__global__ __launch_bounds__(kSchedThreads) void prefill_varlen_schedule_kernel(PrefillParams p,
+                                                                               int* list,
+                                                                               int shift) {
+  __shared__ int hist[kSchedBins];
+  __shared__ int wsum[kSchedThreads / 64];
+  __shared__ int s_cu[kSchedStagedB + 1], s_len[kSchedStagedB];
+  const int t = threadIdx.x;
+  for (int i = t; i < kSchedBins; i += kSchedThreads) hist[i] = 0;
+  if (p.B <= kSchedStagedB) {
+    for (int i = t; i <= p.B; i += kSchedThreads) s_cu[i] = p.cu_seqlens_q[i];
+    for (int i = t; i < p.B; i += kSchedThreads) s_len[i] = p.kv_lens[i];
+    __syncthreads();
+    varlen_schedule<true>(p, list, shift, hist, wsum, s_cu, s_len);
+  } else {
+    __syncthreads();
+    varlen_schedule<false>(p, list, shift, hist, wsum, p.cu_seqlens_q, p.kv_lens);
   }
 }
 
