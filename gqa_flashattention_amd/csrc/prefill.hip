@@ -566,23 +566,37 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   }
 
   // Epilogue: O = O / l, rounded to bf16.  Lane holds, for d-tile dt and
-  // i = 0..15, d = 32*dt + 8*(i/4) + 4*h2 + (i%4) of row qrow.
+  // i = 0..15, d = 32*dt + 8*(i/4) + 4*h2 + (i%4) of row qw0 + c: 8-byte
+  // pieces of 32 rows.  Stored as they are, every store instruction would
+  // touch 32 rows; instead each wave stages its 32 rows (8 KiB, 16-byte
+  // pieces XOR-swizzled by row) in the K ring, which nothing reads any more
+  // (the last group's barrier followed its last use), and copies them out
+  // row-contiguous: 4 whole rows per store instruction.
   const float lsum = lpart + __shfl_xor(lpart, 32, 64);
-  if (qrow < S_q) {
-    const float inv = 1.f / lsum;
-    __bf16* orow = static_cast<__bf16*>(p.o) + (qrow0 + (size_t)qrow * qstride) * kD;
+  const float inv = 1.f / lsum;
+  char* stage = reinterpret_cast<char*>(&sK[0][0]) + wave * (32 * kD * 2);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = 32 * dt + 8 * i4 + 4 * h2;
-        u32x2 v2 = {pack_bf16x2(o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv),
-                    pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d0) = v2;
-      }
-    if (p.lse != nullptr && h2 == 0)
-      p.lse[qrow0 + (size_t)qrow * qstride] = (m_ref + __log2f(lsum)) * kLn2;
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int pc = 4 * dt + i4;   // 16-byte piece of d = 32*dt + 8*i4 .. +8
+      u32x2 v2 = {pack_bf16x2(o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv),
+                  pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv)};
+      *reinterpret_cast<u32x2*>(stage + c * (kD * 2) + 16 * (pc ^ (c & 15)) + 8 * h2) = v2;
+    }
+  {
+    const int pc = lane & 15;
+    __bf16* obase = static_cast<__bf16*>(p.o);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 4 * k + (lane >> 4);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * (kD * 2) + 16 * (pc ^ (r & 15)));
+      if (qw0 + r < S_q)
+        *reinterpret_cast<u32x4*>(obase + (qrow0 + (size_t)(qw0 + r) * qstride) * kD + 8 * pc) = v;
+    }
   }
+  if (qrow < S_q && p.lse != nullptr && h2 == 0)
+    p.lse[qrow0 + (size_t)qrow * qstride] = (m_ref + __log2f(lsum)) * kLn2;
 }
 
 // Tile count of a varlen work item (b, pblk): the key tiles its workgroup

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.skipif(shutil.which(build.hipcc()) is None and not os.p
 # and other epilogue values) live across its main loop without using them
 # inside it; they are stored once before the loop and reloaded once after
 # it (the listing is checked by hand when this changes).
-ALLOWED_SCRATCH = {f"_ZN3gqa19prefill_bf16_kernelILb{v}ELb{pg}EEEvNS_13PrefillParamsE": 32
+ALLOWED_SCRATCH = {f"_ZN3gqa19prefill_bf16_kernelILb{v}ELb{pg}EEEvNS_13PrefillParamsE": 40
                    for v, pg in ((0, 0), (1, 0), (1, 1))}
 
 
