@@ -14,6 +14,9 @@ constexpr int kD = 128;
 constexpr int kMaxG = 16;          // query heads per KV head the decode MFMA tile holds
 constexpr int kF32Chunk = 64;      // keys per split of the fp32 decode path
 constexpr int kBf16ChunkQuantum = 128;  // 4 waves x 32-key blocks
+// Largest explicit split: keeps every per-wave and per-split byte count of
+// the split kernels' 32-bit buffer resources and offsets far from overflow.
+constexpr int kMaxChunk = 1 << 20;
 constexpr int kMultiMaxRows = 128;      // G * T_q rows of the multi-token decode tile
 constexpr size_t kWsAlign = 256;
 
@@ -30,7 +33,7 @@ int split_tokens(int B, int H_kv, int max_kv_len, int chunk_tokens, int dtype) {
   }
   if (dtype != GQA_DTYPE_BF16) return -GQA_ERR_INVALID_ARG;
   if (chunk_tokens > 0) {
-    if (chunk_tokens % kBf16ChunkQuantum != 0) return -GQA_ERR_INVALID_ARG;
+    if (chunk_tokens % kBf16ChunkQuantum != 0 || chunk_tokens > kMaxChunk) return -GQA_ERR_INVALID_ARG;
     return chunk_tokens;
   }
   // About 64 splits of the longest sequence, in multiples of 128 keys,
@@ -63,7 +66,7 @@ int multi_split_tokens(int B, int H_q, int H_kv, int T_q, int max_kv_len, int ch
   if (multi_on_decode_kernel(H_q / H_kv, T_q))
     return split_tokens(B, H_kv, max_kv_len, chunk_tokens, dtype);
   if (chunk_tokens > 0) {
-    if (chunk_tokens % kBf16ChunkQuantum != 0) return -GQA_ERR_INVALID_ARG;
+    if (chunk_tokens % kBf16ChunkQuantum != 0 || chunk_tokens > kMaxChunk) return -GQA_ERR_INVALID_ARG;
     return chunk_tokens;
   }
   // About 32 splits of the longest sequence, in multiples of 128 keys,

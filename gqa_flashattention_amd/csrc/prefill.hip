@@ -248,10 +248,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // rows; one 1 KiB instruction fills a group, lane l landing at physical
   // piece l%16 of row 4*group + l/16 and fetching the logical piece that
   // belongs there.  The loads go through a buffer resource that covers only
-  // the S_kv valid rows of this (sequence, KV head) from the tile on, so
-  // rows past S_kv read as zeros (no clamping, nothing outside the valid
-  // rows is touched); those keys are masked and their zero V rows get
-  // weight 0.  Tile indices past the last tile are clamped to it (the
+  // the tile's valid rows (at most 64, below S_kv), so rows past S_kv read
+  // as zeros (no clamping, nothing outside the valid rows is touched, and
+  // the resource's 32-bit size cannot overflow for any cache length); those
+  // keys are masked and their zero V rows get weight 0.  Tile indices past the last tile are clamped to it (the
   // buffers they fill are never read).
   // Paged form: a wave's two instructions cover rows 8w .. 8w+7 of the
   // tile, which lie in one page (pages hold at least 16 rows, a power of
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       rsrc = buffer_rsrc(reinterpret_cast<const void*>(a), (unsigned)(8 * wv + valid) * (kD * 2));
     } else {
       rsrc = buffer_rsrc((kv ? Vg : Kg) + (size_t)tile * (kBN * kD),
-                         (unsigned)(S_kv - tile * kBN) * (kD * 2));
+                         (unsigned)min(S_kv - tile * kBN, kBN) * (kD * 2));
     }
     dma_load_x4(ld_off[kv][i], rsrc,
                 (kv ? lds_v0 : lds_k0) + buf * kTileBytes + 4 * (kInsts * wave + i) * kD * 2);
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     // Anchor the softmax inputs here, so that no exponential is hoisted
     // out of the sequence.
     asm volatile("" : "+v"(negr));
-    float psum = 0.f;
+    float psum = -0.f;   // -0 + x == x for every x, so the first add folds away
     u32x4 pw[4];
     float ev[32];   // exponentials of S(j), key order of the lane's scores
     Tile16 Sn;

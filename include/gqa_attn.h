@@ -101,8 +101,8 @@ int gqa_attn_version(void);
 /*
  * Number of keys each decode split (one workgroup's contiguous slice of one
  * sequence) covers for these arguments: `chunk_tokens` itself when it is
- * positive (it must then be a multiple of 128 for bf16; the f32 path has a
- * fixed split of 64 keys, so for f32 it must be 64), or the library's
+ * positive (it must then be a multiple of 128 for bf16, at most 2^20; the
+ * f32 path has a fixed split of 64 keys, so for f32 it must be 64), or the library's
  * automatic choice when it is 0.  Splits are contiguous
  * position blocks, the placement the pages require for prefill/decode
  * sharing (§0 "CUBE Group", token-to-rank placement).  Returns a negative
@@ -216,7 +216,7 @@ int gqa_attn_decode_multi(const void* q, const void* k_cache, const void* v_cach
 
 /*
  * Keys per multi-token decode split: `chunk_tokens` when positive (a
- * multiple of 128), else the library's automatic choice (it depends on
+ * multiple of 128, at most 2^20), else the library's automatic choice (it depends on
  * G * T_q, hence H_q).  Returns a negative gqa_status_t on invalid
  * arguments (GQA_ERR_UNSUPPORTED for f32).
  */

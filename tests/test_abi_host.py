@@ -55,6 +55,9 @@ def test_split_tokens_rules():
     assert L.gqa_attn_decode_split_tokens(1, 1, 256, 128, F32) == -INVALID
     assert L.gqa_attn_decode_split_tokens(1, 8, 32768, 384, BF16) == 384
     assert L.gqa_attn_decode_split_tokens(1, 8, 32768, 100, BF16) == -INVALID
+    # Explicit splits are capped at 2^20 keys (32-bit per-wave byte counts).
+    assert L.gqa_attn_decode_split_tokens(1, 8, 1 << 21, 1 << 20, BF16) == 1 << 20
+    assert L.gqa_attn_decode_split_tokens(1, 8, 1 << 21, (1 << 20) + 128, BF16) == -INVALID
     auto = L.gqa_attn_decode_split_tokens(1, 8, 32768, 0, BF16)
     assert auto == 512
     assert L.gqa_attn_decode_split_tokens(4, 8, 131072, 0, BF16) == 1280
@@ -222,6 +225,8 @@ def test_multi_split_and_workspace_rules():
     assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 4, 100, 0, BF16) == 128    # tiny context
     assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 4, 32768, 384, BF16) == 384
     assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 4, 32768, 200, BF16) == -INVALID
+    assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 4, 1 << 21, (1 << 20) + 128,
+                                                BF16) == -INVALID
     assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 4, 32768, 0, F32) == -UNSUPPORTED
     assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 0, 32768, 0, BF16) == -INVALID
     assert L.gqa_attn_decode_multi_split_tokens(1, 64, 8, 9, 8, 0, BF16) == -INVALID   # T_q > L
