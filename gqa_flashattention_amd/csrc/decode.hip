@@ -19,8 +19,9 @@
 // multiply) so the exponentials are single v_exp_f32 instructions.  The 4
 // waves merge through LDS and the workgroup writes one partial.
 //
-// A second kernel merges the partials (one workgroup per sequence and query
-// head).  Merging inside the partial kernel -- the last workgroup to arrive
+// A second kernel merges the partials: one wave per (sequence, query head)
+// and quarter of d, so a row's partials come in through four CUs' load
+// pipelines at once.  Merging inside the partial kernel -- the last workgroup to arrive
 // for a (sequence, KV head) merging the others' partials -- was measured
 // slower on MI355X: publishing partials across the 8 XCDs' separate L2s
 // costs either an L2 write-back per workgroup or agent-coherent accesses,
@@ -458,8 +459,8 @@ __global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p)
   }
 }
 
-// Online log-sum-exp merge of split partials, 16 at a time so that all of a
-// group's loads are in flight together.  (M, acc, lacc) is the running
+// Online log-sum-exp merge of split partials, NG at a time per lane so that
+// all of a group's loads are in flight together.  (M, acc, lacc) is the running
 // state; a group is folded in with the merge rule of §4: rescale both sides
 // to the larger max and add.
 struct MergeAcc {
@@ -468,21 +469,23 @@ struct MergeAcc {
   float lacc;
 };
 
-constexpr int kMergeGroup = 16;
+constexpr int kCombSlots = 8;     // split slots per wave (lane / 8)
 
+template <int NG>   // splits per lane and load round
 struct MergeLoads {
-  float m[kMergeGroup], l[kMergeGroup];
-  f32x4 o[kMergeGroup];
+  float m[NG], l[NG];
+  f32x4 o[NG];
 };
 
 // Loads splits s0, s0 + stride, ...; indices at or past `s_alloc` (the
 // partials the workspace holds per row) re-read the last one, so every load
 // is unconditional and all of them are in flight together.  Such splits lie
 // past the sequence's split count and are discarded by merge_fold.
-__device__ __forceinline__ void merge_load(MergeLoads& g, const float* ml, const float* po, int s0,
+template <int NG>
+__device__ __forceinline__ void merge_load(MergeLoads<NG>& g, const float* ml, const float* po, int s0,
                                            int s_alloc, int stride) {
 #pragma unroll
-  for (int u = 0; u < kMergeGroup; ++u) {
+  for (int u = 0; u < NG; ++u) {
     const int s = min(s0 + u * stride, s_alloc - 1);
     const f32x2 m2 = *reinterpret_cast<const f32x2*>(ml + 2 * s);
     g.o[u] = *reinterpret_cast<const f32x4*>(po + (size_t)s * kD);
@@ -491,12 +494,25 @@ __device__ __forceinline__ void merge_load(MergeLoads& g, const float* ml, const
   }
 }
 
+// Merges (m, acc, l) into `st` with the rule of §4.  Branch-free: with both
+// sides empty (m = -inf) the reference is 0 and both weights are 0.
+__device__ __forceinline__ void merge_pair(MergeAcc& st, float m, f32x4 acc, float l) {
+  const float gm = fmaxf(st.M, m);
+  const float ref = gm == kNegInf ? 0.f : gm;
+  const float c0 = fast_exp2(st.M - ref);
+  const float c1 = fast_exp2(m - ref);
+  st.acc = st.acc * c0 + acc * c1;
+  st.lacc = st.lacc * c0 + l * c1;
+  st.M = gm;
+}
+
 // Folds the loaded splits below `s_valid` (the splits of this call) into
 // `st`; the others are replaced by the identity (-inf, 0, 0) before use.
-__device__ __forceinline__ void merge_fold(MergeAcc& st, MergeLoads& g, int s0, int s_valid,
+template <int NG>
+__device__ __forceinline__ void merge_fold(MergeAcc& st, MergeLoads<NG>& g, int s0, int s_valid,
                                            int stride) {
 #pragma unroll
-  for (int u = 0; u < kMergeGroup; ++u) {
+  for (int u = 0; u < NG; ++u) {
     if (s0 + u * stride >= s_valid) {
       g.m[u] = kNegInf;
       g.l[u] = 0.f;
@@ -505,7 +521,7 @@ __device__ __forceinline__ void merge_fold(MergeAcc& st, MergeLoads& g, int s0, 
   }
   float gm = st.M;
 #pragma unroll
-  for (int u = 0; u < kMergeGroup; ++u) gm = fmaxf(gm, g.m[u]);
+  for (int u = 0; u < NG; ++u) gm = fmaxf(gm, g.m[u]);
   // Branch-free (so that no load is sunk behind a branch): with every side
   // empty, gm = -inf and the weights below are exp2(-inf) = 0.
   const float ref = gm == kNegInf ? 0.f : gm;
@@ -513,7 +529,7 @@ __device__ __forceinline__ void merge_fold(MergeAcc& st, MergeLoads& g, int s0, 
   st.acc *= c;
   st.lacc *= c;
 #pragma unroll
-  for (int u = 0; u < kMergeGroup; ++u) {
+  for (int u = 0; u < NG; ++u) {
     const float w = fast_exp2(g.m[u] - ref);
     st.acc += w * g.o[u];
     st.lacc += w * g.l[u];
@@ -521,54 +537,62 @@ __device__ __forceinline__ void merge_fold(MergeAcc& st, MergeLoads& g, int s0, 
   st.M = gm;
 }
 
-// Combine: one workgroup of 128 threads per (sequence, query head, token); 4
-// groups of 32 threads take every 4th split, thread t covers output columns
-// 4*(t%32) .. +4, and the groups merge through LDS.  Normalises once and
-// rounds to the output dtype (the final O / l of §4).  The first 64 splits'
-// loads are issued together with the sequence length's, so a call of up to
-// 64 splits costs one memory round trip; splits past the sequence's count
-// are discarded after the loads.
-template <typename OutT>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_combine_kernel(DecodeParams p) {
+// Combine: one wave per (output row, quarter of d), rows being (sequence,
+// query head, token); the 4 waves of a row run on different CUs, so a row's
+// partials are fetched by four load pipelines at once.  Lane l takes split
+// slot j = l / 8 (splits j, j + 8, j + 16, ...) and output columns
+// 32*quarter + 4*(l % 8) .. +4; the 8 slots then merge across lanes
+// (xor 8, 16, 32).  Normalises once and rounds to the output dtype (the
+// final O / l of §4).  The first 8*NG splits' loads are issued together with
+// the sequence length's, so a call of up to 8*NG splits costs one memory
+// round trip; splits past the sequence's count are discarded after the
+// loads.  NG (2, 4 or 8) follows the workspace's split count, so that a row
+// with few splits does not load the same partial several times.
+template <typename OutT, int NG>
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
   const int bh = blockIdx.x;                 // folded row (sequence, head, token)
+  const int quarter = blockIdx.y;
   const int b = bh / (p.H_q * p.T_q);
-  const int t = threadIdx.x;
-  const int grp = t >> 5;
-  const int d0 = (t & 31) * 4;
+  const int lane = threadIdx.x;
+  const int slot = lane >> 3;
+  const int d0 = 32 * quarter + 4 * (lane & 7);
   const size_t part0 = (size_t)bh * p.n_split_max;
   const float* ml = p.ws_ml + 2 * part0;
   const float* po = p.ws_o + part0 * kD + d0;
   const int len = p.kv_lens[b];
-  MergeLoads g;
-  merge_load(g, ml, po, grp, p.n_split_max, 4);
+  MergeLoads<NG> g;
+  merge_load(g, ml, po, slot, p.n_split_max, kCombSlots);
   const int L = min(len, p.max_kv_len);
   const int ns = (L + p.chunk - 1) / p.chunk;
   MergeAcc st{kNegInf, {0.f, 0.f, 0.f, 0.f}, 0.f};
-  merge_fold(st, g, grp, ns, 4);
-  for (int s0 = grp + 4 * kMergeGroup; s0 < ns; s0 += 4 * kMergeGroup) {
-    merge_load(g, ml, po, s0, p.n_split_max, 4);
-    merge_fold(st, g, s0, ns, 4);
+  merge_fold(st, g, slot, ns, kCombSlots);
+  for (int s0 = slot + kCombSlots * NG; s0 < ns; s0 += kCombSlots * NG) {
+    merge_load(g, ml, po, s0, p.n_split_max, kCombSlots);
+    merge_fold(st, g, s0, ns, kCombSlots);
   }
-  __shared__ float sm[4], sl[4];
-  __shared__ f32x4 so[4][32];
-  if ((t & 31) == 0) { sm[grp] = st.M; sl[grp] = st.lacc; }
-  so[grp][t & 31] = st.acc;
-  __syncthreads();
-  if (grp == 0) {
-    float MM = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-    for (int g2 = 0; g2 < 4; ++g2) {
-      const float w = sm[g2] == kNegInf ? 0.f : fast_exp2(sm[g2] - MM);
-      a += w * so[g2][t];
-      l += w * sl[g2];
-    }
-    const float inv = 1.f / l;
+#pragma unroll
+  for (int mask = 8; mask < 64; mask <<= 1) {
+    f32x4 ao;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ao[i] = __shfl_xor(st.acc[i], mask, 64);
+    const float mo = __shfl_xor(st.M, mask, 64);
+    const float lo = __shfl_xor(st.lacc, mask, 64);
+    merge_pair(st, mo, ao, lo);
+  }
+  if (slot == 0) {
+    const float inv = 1.f / st.lacc;
     OutT* o = static_cast<OutT*>(p.o) + (size_t)bh * kD + d0;
-    for (int i = 0; i < 4; ++i) o[i] = (OutT)(a[i] * inv);
-    if (p.lse != nullptr && t == 0) p.lse[bh] = (MM + __log2f(l)) * kLn2;
+    if constexpr (sizeof(OutT) == 2) {
+      const u32x2 w = {pack_bf16x2(st.acc[0] * inv, st.acc[1] * inv),
+                       pack_bf16x2(st.acc[2] * inv, st.acc[3] * inv)};
+      *reinterpret_cast<u32x2*>(o) = w;
+    } else {
+      *reinterpret_cast<f32x4*>(o) = st.acc * inv;
+    }
+    if (p.lse != nullptr && lane == 0 && quarter == 0) p.lse[bh] = (st.M + __log2f(st.lacc)) * kLn2;
   }
 }
+
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, int phases) {
   if (phases & kDecodePartial) {
     dim3 grid(p.n_split_max, p.H_kv, p.B);
@@ -584,10 +608,16 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, i
     if (e != hipSuccess) return e;
   }
   if (phases & kDecodeCombine) {
+    const dim3 grid(p.B * p.H_q * p.T_q, 4);
+    const int ng = p.n_split_max <= 16 ? 2 : p.n_split_max <= 32 ? 4 : 8;
     if (bf16) {
-      hipLaunchKernelGGL(decode_combine_kernel<__bf16>, dim3(p.B * p.H_q * p.T_q), dim3(128), 0, stream, p);
+      if (ng == 2) hipLaunchKernelGGL((decode_combine_kernel<__bf16, 2>), grid, dim3(64), 0, stream, p);
+      else if (ng == 4) hipLaunchKernelGGL((decode_combine_kernel<__bf16, 4>), grid, dim3(64), 0, stream, p);
+      else hipLaunchKernelGGL((decode_combine_kernel<__bf16, 8>), grid, dim3(64), 0, stream, p);
     } else {
-      hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(p.B * p.H_q * p.T_q), dim3(128), 0, stream, p);
+      if (ng == 2) hipLaunchKernelGGL((decode_combine_kernel<float, 2>), grid, dim3(64), 0, stream, p);
+      else if (ng == 4) hipLaunchKernelGGL((decode_combine_kernel<float, 4>), grid, dim3(64), 0, stream, p);
+      else hipLaunchKernelGGL((decode_combine_kernel<float, 8>), grid, dim3(64), 0, stream, p);
     }
   }
   return hipGetLastError();
