@@ -344,6 +344,9 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
 // partial over the split, the "fits in scratch" shape of §5.2).
 constexpr int kF32Chunk = 64;
 
+// QS = ceil(G / 4): query slots per thread in the score phase (2*QS in P.V),
+// so that no thread computes rows past the group's G heads.
+template <int QS>
 __global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p) {
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -401,15 +404,17 @@ __global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p)
   {
     const int j = t & (kF32Chunk - 1);
     const int n0 = t >> 6;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[QS];
+#pragma unroll
+    for (int u = 0; u < QS; ++u) acc[u] = 0.f;
 #pragma unroll 16
     for (int d = 0; d < kD; ++d) {
       const float kd = sk[j][d];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] = __builtin_fmaf(sq[n0 + 4 * u][d], kd, acc[u]);   // rows >= G unused
+      for (int u = 0; u < QS; ++u) acc[u] = __builtin_fmaf(sq[n0 + 4 * u][d], kd, acc[u]);   // rows >= G unused
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < QS; ++u) {
       const int n = n0 + 4 * u;
       if (n < p.G) ss[n][j] = j < cnt ? acc[u] * p.scale_log2 : kNegInf;
     }
@@ -438,15 +443,17 @@ __global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p)
   const int dd = t & (kD - 1);
   const int n0 = t >> 7;
   const size_t part0 = ((size_t)b * p.H_q + (size_t)kvh * p.G) * p.n_split_max + split;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc[2 * QS];
+#pragma unroll
+  for (int u = 0; u < 2 * QS; ++u) acc[u] = 0.f;
 #pragma unroll 8
   for (int j = 0; j < kF32Chunk; ++j) {
     const float vj = sv[j][dd];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = __builtin_fmaf(ss[n0 + 2 * u][j], vj, acc[u]);   // rows >= G unused
+    for (int u = 0; u < 2 * QS; ++u) acc[u] = __builtin_fmaf(ss[n0 + 2 * u][j], vj, acc[u]);   // rows >= G unused
   }
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < 2 * QS; ++u) {
     const int n = n0 + 2 * u;
     if (n < p.G) {
       const size_t part = part0 + (size_t)n * p.n_split_max;
@@ -602,7 +609,12 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, i
       else
         hipLaunchKernelGGL(decode_partial_bf16_kernel<false>, grid, dim3(256), 0, stream, p);
     } else {
-      hipLaunchKernelGGL(decode_partial_f32_kernel, grid, dim3(256), 0, stream, p);
+      switch ((p.G + 3) / 4) {
+        case 1: hipLaunchKernelGGL(decode_partial_f32_kernel<1>, grid, dim3(256), 0, stream, p); break;
+        case 2: hipLaunchKernelGGL(decode_partial_f32_kernel<2>, grid, dim3(256), 0, stream, p); break;
+        case 3: hipLaunchKernelGGL(decode_partial_f32_kernel<3>, grid, dim3(256), 0, stream, p); break;
+        default: hipLaunchKernelGGL(decode_partial_f32_kernel<4>, grid, dim3(256), 0, stream, p); break;
+      }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
