@@ -58,12 +58,16 @@ SMALL = [
     (1, 64, 8, (4097,), 4100, "bf16", 0),
     (2, 8, 4, (1, 700), 701, "f32", 0),
     (1, 16, 2, (513,), 513, "f32", 0),
+    # fp32 split kernel: 1, 3 and 4 query slots per thread (G = 1, 12, 16)
+    (1, 3, 3, (100,), 100, "f32", 0),
+    (1, 12, 1, (200,), 200, "f32", 0),
+    (2, 32, 2, (65, 130), 130, "f32", 0),
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}_Hq{c[1]}_Hkv{c[2]}_L{c[3]}_{c[5]}_c{c[6]}")
 def test_decode_shapes(case):
-    """Several tiles plus a ragged tail, G in {1,2,4,8,16}, NaN-padded caches."""
+    """Several tiles plus a ragged tail, G in {1,2,4,8,12,16}, NaN-padded caches."""
     B, H_q, H_kv, lens, cap, dt, chunk = case
     w = inputs.Workload("t", "decode", B=B, H_q=H_q, H_kv=H_kv, d=128, dtype=dt, lens=lens,
                         kv_cap=cap)
