@@ -62,6 +62,8 @@ SMALL = [
     (1, 3, 3, (100,), 100, "f32", 0),
     (1, 12, 1, (200,), 200, "f32", 0),
     (2, 32, 2, (65, 130), 130, "f32", 0),
+    # fp32 with 79 splits: the combine's second load round
+    (1, 8, 1, (5000,), 5000, "f32", 0),
 ]
 
 
