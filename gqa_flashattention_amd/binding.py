@@ -120,6 +120,44 @@ def _require_gpu(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _expect(t, name, shape, dtype, device):
+    """Check one tensor argument on the host before any pointer reaches the
+    library: a wrong shape, dtype, device or stride would otherwise become an
+    out-of-bounds device access instead of an error."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _expect_workspace(ws, device, need):
+    """A caller-supplied workspace: contiguous, on the device, at least
+    ``need`` bytes (the library checks the size too)."""
+    _expect(ws, "workspace", None, None, device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, "
+                         f"{need} needed")
+
+
+def _check_kv(q, k, v, batch):
+    """K and V: 4-D, the same shape, q's dtype and device, ``d`` of q and
+    batch ``batch`` (None: not checked, e.g. a page pool)."""
+    if k.dim() != 4:
+        raise ValueError(f"k must be 4-D, got shape {tuple(k.shape)}")
+    _expect(k, "k", None, q.dtype, q.device)
+    _expect(v, "v", k.shape, q.dtype, q.device)
+    if k.shape[3] != q.shape[-1]:
+        raise ValueError(f"k/v head dimension {k.shape[3]} differs from q's {q.shape[-1]}")
+    if batch is not None and k.shape[0] != batch:
+        raise ValueError(f"k/v hold {k.shape[0]} sequences, q has {batch}")
+
+
 def decode_split_tokens(B, H_kv, max_kv_len, chunk_tokens=0, dtype=DTYPE_BF16) -> int:
     r = lib().gqa_attn_decode_split_tokens(B, H_kv, max_kv_len, chunk_tokens, dtype)
     if r < 0:
@@ -144,21 +182,27 @@ def decode(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chunk_toke
     (``gqa_attn_decode_partial`` / ``_combine``; pass the same ``workspace``
     to both).  Returns ``o`` (and ``lse`` when ``return_lse``).
     """
-    _require_gpu(q, k_cache, v_cache, kv_lens)
+    _require_gpu(q)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B, H_q, d], got shape {tuple(q.shape)}")
     B, H_q, d = q.shape
+    dt = _dtype_code(q)
+    _check_kv(q, k_cache, v_cache, B)
     _, H_kv, kv_cap, _ = k_cache.shape
-    if kv_lens.dtype != torch.int32:
-        raise TypeError("kv_lens must be int32")
+    _expect(kv_lens, "kv_lens", (B,), torch.int32, q.device)
     max_kv_len = kv_cap if max_kv_len is None else int(max_kv_len)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, "out", q.shape, q.dtype, q.device)
     if return_lse and lse is None:
         lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    if return_lse:
+        _expect(lse, "lse", (B, H_q), torch.float32, q.device)
     need = decode_workspace_bytes(B, H_q, H_kv, d, max_kv_len, chunk_tokens, dt)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device, need)
     fn = {"both": "gqa_attn_decode", "partial": "gqa_attn_decode_partial",
           "combine": "gqa_attn_decode_combine"}[phase]
     st = getattr(lib(), fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens), _ptr(out),
@@ -198,21 +242,27 @@ def decode_multi(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chun
     for :func:`decode`.  Returns ``o`` (and ``lse`` ``[B,H_q,T_q]`` when
     ``return_lse``).
     """
-    _require_gpu(q, k_cache, v_cache, kv_lens)
+    _require_gpu(q)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H_q, T_q, d], got shape {tuple(q.shape)}")
     B, H_q, T_q, d = q.shape
+    dt = _dtype_code(q)
+    _check_kv(q, k_cache, v_cache, B)
     _, H_kv, kv_cap, _ = k_cache.shape
-    if kv_lens.dtype != torch.int32:
-        raise TypeError("kv_lens must be int32")
+    _expect(kv_lens, "kv_lens", (B,), torch.int32, q.device)
     max_kv_len = kv_cap if max_kv_len is None else int(max_kv_len)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, "out", q.shape, q.dtype, q.device)
     if return_lse and lse is None:
         lse = torch.empty((B, H_q, T_q), dtype=torch.float32, device=q.device)
+    if return_lse:
+        _expect(lse, "lse", (B, H_q, T_q), torch.float32, q.device)
     need = decode_multi_workspace_bytes(B, H_q, H_kv, d, T_q, max_kv_len, chunk_tokens, dt)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device, need)
     fn = {"both": "gqa_attn_decode_multi", "partial": "gqa_attn_decode_multi_partial",
           "combine": "gqa_attn_decode_multi_combine"}[phase]
     st = getattr(lib(), fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens), _ptr(out),
@@ -250,21 +300,30 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, max_kv_len, scale=No
     bf16; block_table ``[B,max_pages]`` and kv_lens ``[B]`` int32 on the
     device.  Returns ``o`` (and ``lse`` ``[B,H_q,T_q]`` when ``return_lse``).
     """
-    _require_gpu(q, k_pages, v_pages, block_table, kv_lens)
+    _require_gpu(q)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H_q, T_q, d], got shape {tuple(q.shape)}")
     B, H_q, T_q, d = q.shape
-    num_pages, H_kv, page_size, _ = k_pages.shape
-    if block_table.dtype != torch.int32 or kv_lens.dtype != torch.int32:
-        raise TypeError("block_table and kv_lens must be int32")
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dt = _dtype_code(q)
+    _check_kv(q, k_pages, v_pages, None)
+    num_pages, H_kv, page_size, _ = k_pages.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B={B}, max_pages], got {tuple(block_table.shape)}")
+    _expect(block_table, "block_table", None, torch.int32, q.device)
+    _expect(kv_lens, "kv_lens", (B,), torch.int32, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, "out", q.shape, q.dtype, q.device)
     if return_lse and lse is None:
         lse = torch.empty((B, H_q, T_q), dtype=torch.float32, device=q.device)
+    if return_lse:
+        _expect(lse, "lse", (B, H_q, T_q), torch.float32, q.device)
     need = decode_paged_workspace_bytes(B, H_q, H_kv, d, T_q, page_size, max_kv_len,
                                         chunk_tokens, dt)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device, need)
     fn = {"both": "gqa_attn_decode_paged", "partial": "gqa_attn_decode_paged_partial",
           "combine": "gqa_attn_decode_paged_combine"}[phase]
     st = getattr(lib(), fn)(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
@@ -287,12 +346,17 @@ def merge(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, return_lse=False, stre
         raise ValueError("o_a, o_b must be [..., d] and lse_a, lse_b their [...] LSEs")
     if o_a.dtype != o_b.dtype or lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32:
         raise TypeError("O inputs share one dtype; LSEs are float32")
+    for t, n in ((lse_a, "lse_a"), (o_b, "o_b"), (lse_b, "lse_b")):
+        _expect(t, n, None, None, o_a.device)
     d = o_a.shape[-1]
     rows = lse_a.numel()
     if out is None:
         out = torch.empty_like(o_a)
+    _expect(out, "out", o_a.shape, o_a.dtype, o_a.device)
     if return_lse and lse_out is None:
         lse_out = torch.empty_like(lse_a)
+    if lse_out is not None:
+        _expect(lse_out, "lse_out", lse_a.shape, torch.float32, o_a.device)
     st = lib().gqa_attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out),
                               _ptr(lse_out) if (return_lse or lse_out is not None) else None,
                               rows, d, _dtype_code(o_a), _stream(stream))
@@ -307,16 +371,22 @@ def prefill(q, k, v, S_kv=None, causal=True, causal_offset=0, scale=None, return
     q ``[B,H_q,S_q,d]``, k/v ``[B,H_kv,kv_cap,d]`` bf16.  ``S_kv`` defaults to
     ``kv_cap``.  Returns ``o`` (and ``lse`` when ``return_lse``).
     """
-    _require_gpu(q, k, v)
+    _require_gpu(q)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H_q, S_q, d], got shape {tuple(q.shape)}")
     B, H_q, S_q, d = q.shape
+    dt = _dtype_code(q)
+    _check_kv(q, k, v, B)
     _, H_kv, kv_cap, _ = k.shape
     S_kv = kv_cap if S_kv is None else int(S_kv)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, "out", q.shape, q.dtype, q.device)
     if return_lse and lse is None:
         lse = torch.empty((B, H_q, S_q), dtype=torch.float32, device=q.device)
+    if return_lse:
+        _expect(lse, "lse", (B, H_q, S_q), torch.float32, q.device)
     st = lib().gqa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                 _ptr(lse) if return_lse else None, B, H_q, H_kv, d, S_q, S_kv,
                                 kv_cap, int(bool(causal)), int(causal_offset), scale, dt,
@@ -343,23 +413,28 @@ def prefill_varlen(q, k, v, cu_seqlens_q, kv_lens, max_seqlen_q, max_kv_len=None
     tensor, allocated when None) holds the work list.  Returns ``o`` (and
     ``lse`` ``[total_q,H_q]`` when ``return_lse``).
     """
-    _require_gpu(q, k, v, cu_seqlens_q, kv_lens)
+    _require_gpu(q)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [total_q, H_q, d], got shape {tuple(q.shape)}")
     total_q, H_q, d = q.shape
+    dt = _dtype_code(q)
+    _check_kv(q, k, v, None)
     B, H_kv, kv_cap, _ = k.shape
-    if cu_seqlens_q.dtype != torch.int32 or kv_lens.dtype != torch.int32:
-        raise TypeError("cu_seqlens_q and kv_lens must be int32")
-    if cu_seqlens_q.numel() != B + 1 or kv_lens.numel() != B:
-        raise ValueError("cu_seqlens_q must hold B+1 entries and kv_lens B")
+    _expect(cu_seqlens_q, "cu_seqlens_q", (B + 1,), torch.int32, q.device)
+    _expect(kv_lens, "kv_lens", (B,), torch.int32, q.device)
     max_kv_len = kv_cap if max_kv_len is None else int(max_kv_len)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, "out", q.shape, q.dtype, q.device)
     if return_lse and lse is None:
         lse = torch.empty((total_q, H_q), dtype=torch.float32, device=q.device)
+    if return_lse:
+        _expect(lse, "lse", (total_q, H_q), torch.float32, q.device)
+    need = prefill_varlen_workspace_bytes(B, H_q, H_kv, int(max_seqlen_q))
     if workspace is None:
-        need = prefill_varlen_workspace_bytes(B, H_q, H_kv, int(max_seqlen_q))
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device, need)
     st = lib().gqa_attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
                                        _ptr(kv_lens), _ptr(out),
                                        _ptr(lse) if return_lse else None, B, H_q, H_kv, d,
@@ -380,25 +455,32 @@ def prefill_paged(q, k_pages, v_pages, block_table, cu_seqlens_q, kv_lens, max_s
     bf16 and block_table ``[B,max_pages]`` int32 on the device; ``max_kv_len``
     defaults to ``max_pages * page``.
     """
-    _require_gpu(q, k_pages, v_pages, block_table, cu_seqlens_q, kv_lens)
+    _require_gpu(q)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [total_q, H_q, d], got shape {tuple(q.shape)}")
     total_q, H_q, d = q.shape
+    dt = _dtype_code(q)
+    _check_kv(q, k_pages, v_pages, None)
     num_pages, H_kv, page, _ = k_pages.shape
+    if block_table.dim() != 2:
+        raise ValueError(f"block_table must be [B, max_pages], got {tuple(block_table.shape)}")
+    _expect(block_table, "block_table", None, torch.int32, q.device)
     B, max_pages = block_table.shape
-    for t in (block_table, cu_seqlens_q, kv_lens):
-        if t.dtype != torch.int32:
-            raise TypeError("block_table, cu_seqlens_q and kv_lens must be int32")
-    if cu_seqlens_q.numel() != B + 1 or kv_lens.numel() != B:
-        raise ValueError("cu_seqlens_q must hold B+1 entries and kv_lens B")
+    _expect(cu_seqlens_q, "cu_seqlens_q", (B + 1,), torch.int32, q.device)
+    _expect(kv_lens, "kv_lens", (B,), torch.int32, q.device)
     max_kv_len = max_pages * page if max_kv_len is None else int(max_kv_len)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, "out", q.shape, q.dtype, q.device)
     if return_lse and lse is None:
         lse = torch.empty((total_q, H_q), dtype=torch.float32, device=q.device)
+    if return_lse:
+        _expect(lse, "lse", (total_q, H_q), torch.float32, q.device)
+    need = prefill_varlen_workspace_bytes(B, H_q, H_kv, int(max_seqlen_q))
     if workspace is None:
-        need = prefill_varlen_workspace_bytes(B, H_q, H_kv, int(max_seqlen_q))
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device, need)
     st = lib().gqa_attn_prefill_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                                       _ptr(cu_seqlens_q), _ptr(kv_lens), _ptr(out),
                                       _ptr(lse) if return_lse else None, B, H_q, H_kv, d, total_q,

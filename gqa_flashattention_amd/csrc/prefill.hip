@@ -105,27 +105,59 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   __shared__ int sPage[kPaged ? kPrefillMaxPages : 1];
   __shared__ __attribute__((aligned(1024))) __bf16 sV[kBufs][kTileElems];
 
-  // Workgroup -> (position block, sequence, head group, KV head).
-  const int hpw = p.heads_per_wg;
-  const int pbw = kWaves / hpw;          // 32-position blocks per workgroup
-  const int ngroups = p.G / hpw;
-  int id = blockIdx.x;
-  const int kvh = id % p.H_kv;
-  id /= p.H_kv;
-  const int hg = id % ngroups;
-  id /= ngroups;
-  int b, pblk;
-  if constexpr (kVarlen) {
-    // Work-list entry b * n_qblk + pblk, clamped into range.
-    const unsigned n_items = (unsigned)p.B * (unsigned)p.n_qblk;
-    const unsigned item = min((unsigned)p.sched[id], n_items - 1u);
-    b = (int)(item / (unsigned)p.n_qblk);
-    pblk = (int)(item % (unsigned)p.n_qblk);
-  } else {
-    b = id % p.B;
-    id /= p.B;
-    pblk = p.n_qblk - 1 - id;
-  }
+  // Workgroup and wave -> (sequence, position block, query head, KV head),
+  // this sequence's chunk length, key count and causal offset, and the
+  // addressing of the wave's query rows: row i of head h is row
+  // `qrow0 + i * qstride` of the [rows, d] view of q, o and lse.  Varlen
+  // sizes come from device arrays and are clamped, so a malformed array
+  // cannot move any access outside the buffers (it only makes the results
+  // meaningless).  The epilogue evaluates this again from opaque copies of
+  // the ids instead of keeping the results live across the main loop.
+  struct Place {
+    int b, kvh, h, P0, qw0, S_q, S_kv, offset, qstride;
+    size_t qrow0;
+  };
+  auto locate = [&](const PrefillParams& p, int bid, int wave_u) -> Place {
+    Place L;
+    const int hpw = p.heads_per_wg;
+    const int ngroups = p.G / hpw;
+    int id = bid;
+    L.kvh = id % p.H_kv;
+    id /= p.H_kv;
+    const int hg = id % ngroups;
+    id /= ngroups;
+    int pblk;
+    if constexpr (kVarlen) {
+      // Work-list entry b * n_qblk + pblk, clamped into range.
+      const unsigned n_items = (unsigned)p.B * (unsigned)p.n_qblk;
+      const unsigned item = min((unsigned)p.sched[id], n_items - 1u);
+      L.b = (int)(item / (unsigned)p.n_qblk);
+      pblk = (int)(item % (unsigned)p.n_qblk);
+    } else {
+      L.b = id % p.B;
+      id /= p.B;
+      pblk = p.n_qblk - 1 - id;
+    }
+    L.h = L.kvh * p.G + hg * hpw + wave_u % hpw;
+    L.P0 = pblk * 32 * (kWaves / hpw);
+    L.qw0 = L.P0 + 32 * (wave_u / hpw);   // first row of this wave
+    if constexpr (kVarlen) {
+      const int t0 = min(max(p.cu_seqlens_q[L.b], 0), p.S_q);
+      const int t1 = min(max(p.cu_seqlens_q[L.b + 1], t0), p.S_q);
+      L.S_q = t1 - t0;
+      L.S_kv = min(max(p.kv_lens[L.b], 0), p.S_kv);
+      L.offset = p.causal ? max(L.S_kv - L.S_q, 0) : 0;
+      L.qrow0 = (size_t)t0 * p.H_q + L.h;
+      L.qstride = p.H_q;
+    } else {
+      L.S_q = p.S_q;
+      L.S_kv = p.S_kv;
+      L.offset = p.offset;
+      L.qrow0 = ((size_t)L.b * p.H_q + L.h) * p.S_q;
+      L.qstride = 1;
+    }
+    return L;
+  };
 
   const int t = threadIdx.x;
   const int wave = t >> 6;
@@ -134,43 +166,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int h2 = lane >> 5;      // half of the wave
   const int t16 = lane & 15;
   const int gamma = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
-  const int h = kvh * p.G + hg * hpw + wave % hpw;
-  const int P0 = pblk * 32 * pbw;
-  const int qw0 = P0 + 32 * (wave / hpw);   // first row of this wave
-  const int qrow = qw0 + c;                 // this lane's query row
+  const Place pl = locate(p, blockIdx.x, wv);
+  const int b = pl.b, kvh = pl.kvh, P0 = pl.P0, qw0 = pl.qw0;
+  const int S_q = pl.S_q, S_kv = pl.S_kv, offset = pl.offset, qstride = pl.qstride;
+  const size_t qrow0 = pl.qrow0;
+  const int pbw = kWaves / p.heads_per_wg;   // 32-position blocks per workgroup
+  const int qrow = qw0 + c;                   // this lane's query row
 
-  // This sequence's chunk length, key count and causal offset; query row i
-  // of head h is row `qrow0 + i * qstride` of the [rows, d] view of q, o
-  // and lse.  Varlen sizes come from device arrays and are clamped, so a
-  // malformed array cannot move any access outside the buffers (it only
-  // makes the results meaningless).
-  int S_q, S_kv, offset, qstride;
-  size_t qrow0;
-  if constexpr (kVarlen) {
-    const int t0 = min(max(p.cu_seqlens_q[b], 0), p.S_q);
-    const int t1 = min(max(p.cu_seqlens_q[b + 1], t0), p.S_q);
-    S_q = t1 - t0;
-    S_kv = min(max(p.kv_lens[b], 0), p.S_kv);
-    offset = p.causal ? max(S_kv - S_q, 0) : 0;
-    qrow0 = (size_t)t0 * p.H_q + h;
-    qstride = p.H_q;
-  } else {
-    S_q = p.S_q;
-    S_kv = p.S_kv;
-    offset = p.offset;
-    qrow0 = ((size_t)b * p.H_q + h) * p.S_q;
-    qstride = 1;
-  }
   if (P0 >= S_q) return;   // the whole workgroup: past this chunk's end
-  if (S_kv == 0) {
-    // No key (an empty sequence, varlen only): O = 0, lse = -inf, the
-    // convention for a row that sees nothing.
-    if (qrow < S_q) {
-      __bf16* orow = static_cast<__bf16*>(p.o) + (qrow0 + (size_t)qrow * qstride) * kD;
-      for (int d0 = 4 * h2; d0 < kD; d0 += 8)
+  if (kVarlen && S_kv == 0) {
+    // No key (an empty sequence, varlen only: the dense launch has
+    // S_kv >= 1): O = 0, lse = -inf, the convention for a row that sees
+    // nothing.  The rows are addressed from opaque copies of the ids, as in
+    // the epilogue: this block is laid out after the main loop, and values
+    // shared with the loop's prologue would otherwise stay live across it.
+    int tid_z = threadIdx.x, bid_z = blockIdx.x;
+    asm volatile("" : "+v"(tid_z), "+s"(bid_z));
+    const Place pz = locate(p, bid_z, __builtin_amdgcn_readfirstlane(tid_z >> 6));
+    const int qrow_z = pz.qw0 + (tid_z & 31), h2_z = (tid_z >> 5) & 1;
+    if (qrow_z < pz.S_q) {
+      __bf16* orow = static_cast<__bf16*>(p.o) + (pz.qrow0 + (size_t)qrow_z * pz.qstride) * kD;
+      for (int d0 = 4 * h2_z; d0 < kD; d0 += 8)
         *reinterpret_cast<u32x2*>(orow + d0) = u32x2{0, 0};
-      if (p.lse != nullptr && h2 == 0) p.lse[qrow0 + (size_t)qrow * qstride] = kNegInf;
+      if (p.lse != nullptr && h2_z == 0) p.lse[pz.qrow0 + (size_t)qrow_z * pz.qstride] = kNegInf;
     }
     return;
   }
@@ -192,7 +212,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const size_t kv_base = kPaged ? 0 : ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD;
   const __bf16* Kg = static_cast<const __bf16*>(p.k) + kv_base;
   const __bf16* Vg = static_cast<const __bf16*>(p.v) + kv_base;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   // Q^T operand (B of S^T): query qrow, d = 16*ks + 8*h2 .. +8.  A negative
   // scale is applied exactly by flipping Q's sign bits.
@@ -316,6 +335,34 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
         T.s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_opnd(kb, mt, ks), qb[ks],
                                                           ks ? T.s[mt] : zero, 0, 0, 0);
       }
+  };
+
+  // S^T of tile `tile` with the K operands read from global memory (the
+  // rare fix-up path): the same operand values and MFMA sequence as
+  // compute_s, so the scores are bit-identical, but no LDS slot is read --
+  // the waves are not synchronised between the two steps of a group, and
+  // another wave may already be refilling the slot that held this tile.
+  // Rows past S_kv read row S_kv - 1 (in bounds); their scores are masked.
+  auto compute_s_global = [&](Tile16& T, int tile) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int row = min(tile * kBN + 32 * mt + c, S_kv - 1);
+      const __bf16* kr;
+      if constexpr (kPaged) {
+        const int lp = min(row >> p.page_shift, min(p.max_pages, kPrefillMaxPages) - 1);
+        kr = Kg + ((size_t)sPage[lp] * p.H_kv + kvh) * ((size_t)kD << p.page_shift) +
+             (size_t)(row & ((1 << p.page_shift) - 1)) * kD;
+      } else {
+        kr = Kg + (size_t)row * kD;
+      }
+      kr += 8 * h2;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const f32x16 zero = {};
+        T.s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kr + 16 * ks)), qb[ks],
+                                                          ks ? T.s[mt] : zero, 0, 0, 0);
+      }
+    }
   };
 
   f32x16 o[4];
@@ -518,15 +565,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // The softmax uses the current reference; if any weight exceeds 2^64
   // (some score is more than 64 above the reference: rare once the
   // prologue has set it from tile 0) the lane sum shows it, and the tile's
-  // scores are recomputed from K (still in LDS), the reference moved and P
-  // redone.
+  // scores are recomputed from K in global memory, the reference moved and
+  // P redone.
   auto step = [&](auto kbuf, auto vbuf, PTile& pprev, PTile& pcur, int j, const int (*ld)[4]) {
-    constexpr int kb = decltype(kbuf)::value;   // K buffer of tile j+1
     if (j >= n_full) mask_tile(T, j);
     float psum = mma_step(kbuf, vbuf, T, pprev, pcur, ld);
     if (__any(!(psum <= kPsumLimit))) {
       Tile16 Tj;
-      compute_s(Tj, (kb + 3) % 4);            // K buffer of tile j
+      compute_s_global(Tj, j);
       if (j >= n_full) mask_tile(Tj, j);
       const float hmax = fmaxf(half_max(Tj.s[0]), half_max(Tj.s[1]));
       move_ref(hmax * sl2);
@@ -572,9 +618,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // pieces XOR-swizzled by row) in the K ring, which nothing reads any more
   // (the last group's barrier followed its last use), and copies them out
   // row-contiguous: 4 whole rows per store instruction.
+  // The ids and the kernel arguments are re-read through opaque copies (the
+  // arguments from the kernarg segment, where this kernel's only argument
+  // sits at offset 0), so the row addressing is recomputed here rather than
+  // held in registers through the loop.
+  int tid_e = threadIdx.x, bid_e = blockIdx.x;
+  const PrefillParams* pk =
+      reinterpret_cast<const PrefillParams*>(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+v"(tid_e), "+s"(bid_e), "+s"(pk));
+  const int lane_e = tid_e & 63, c_e = tid_e & 31, h2_e = (tid_e >> 5) & 1;
+  const int wave_e = __builtin_amdgcn_readfirstlane(tid_e >> 6);
+  const Place pe = locate(*pk, bid_e, wave_e);
   const float lsum = lpart + __shfl_xor(lpart, 32, 64);
   const float inv = 1.f / lsum;
-  char* stage = reinterpret_cast<char*>(&sK[0][0]) + wave * (32 * kD * 2);
+  char* stage = reinterpret_cast<char*>(&sK[0][0]) + wave_e * (32 * kD * 2);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -582,21 +639,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       const int pc = 4 * dt + i4;   // 16-byte piece of d = 32*dt + 8*i4 .. +8
       u32x2 v2 = {pack_bf16x2(o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv),
                   pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv)};
-      *reinterpret_cast<u32x2*>(stage + c * (kD * 2) + 16 * (pc ^ (c & 15)) + 8 * h2) = v2;
+      *reinterpret_cast<u32x2*>(stage + c_e * (kD * 2) + 16 * (pc ^ (c_e & 15)) + 8 * h2_e) = v2;
     }
   {
-    const int pc = lane & 15;
-    __bf16* obase = static_cast<__bf16*>(p.o);
+    const int pc = lane_e & 15;
+    __bf16* obase = static_cast<__bf16*>(pk->o);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int r = 4 * k + (lane >> 4);
+      const int r = 4 * k + (lane_e >> 4);
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * (kD * 2) + 16 * (pc ^ (r & 15)));
-      if (qw0 + r < S_q)
-        *reinterpret_cast<u32x4*>(obase + (qrow0 + (size_t)(qw0 + r) * qstride) * kD + 8 * pc) = v;
+      if (pe.qw0 + r < pe.S_q)
+        *reinterpret_cast<u32x4*>(obase + (pe.qrow0 + (size_t)(pe.qw0 + r) * pe.qstride) * kD +
+                                  8 * pc) = v;
     }
   }
-  if (qrow < S_q && p.lse != nullptr && h2 == 0)
-    p.lse[qrow0 + (size_t)qrow * qstride] = (m_ref + __log2f(lsum)) * kLn2;
+  const int qrow_e = pe.qw0 + c_e;
+  if (qrow_e < pe.S_q && pk->lse != nullptr && h2_e == 0)
+    pk->lse[pe.qrow0 + (size_t)qrow_e * pe.qstride] = (m_ref + __log2f(lsum)) * kLn2;
 }
 
 // Tile count of a varlen work item (b, pblk): the key tiles its workgroup

@@ -228,7 +228,9 @@ def scatter_pages(w: Workload, k, v, page_size: int, seed: int, spare_pages: int
     physical pages in a seeded random order (generator ``seed*16 + 4``),
     ``spare_pages`` extra pages are NaN, table entries past a sequence's
     pages name a NaN page, and rows of a last page past the length are NaN.
-    Returns the K and V pools and the block table ``[B, max_pages]`` int32."""
+    The pools are built on the host and uploaded with one copy each (no
+    per-page device copies).  Returns the K and V pools and the block table
+    ``[B, max_pages]`` int32."""
     max_pages = (w.kv_cap + page_size - 1) // page_size
     need = [(L + page_size - 1) // page_size for L in w.lens]
     num_pages = sum(need) + spare_pages
@@ -236,19 +238,22 @@ def scatter_pages(w: Workload, k, v, page_size: int, seed: int, spare_pages: int
     perm = torch.randperm(num_pages, generator=g)
     nan_page = int(perm[-1])
     table = torch.full((w.B, max_pages), nan_page, dtype=torch.int32)
-    k_pages = torch.full((num_pages, w.H_kv, page_size, w.d), float("nan"), dtype=w.torch_dtype,
-                         device=device)
-    v_pages = torch.full_like(k_pages, float("nan"))
-    nxt = 0
-    for b, L in enumerate(w.lens):
-        for lp in range(need[b]):
-            pp = int(perm[nxt])
-            nxt += 1
-            table[b, lp] = pp
-            rows = min(page_size, L - lp * page_size)
-            k_pages[pp, :, :rows] = k[b, :, lp * page_size:lp * page_size + rows]
-            v_pages[pp, :, :rows] = v[b, :, lp * page_size:lp * page_size + rows]
-    return k_pages, v_pages, table.to(device)
+    pools = []
+    for src in (k, v):
+        src = src.cpu()
+        pool = torch.full((num_pages, w.H_kv, page_size, w.d), float("nan"), dtype=w.torch_dtype)
+        nxt = 0
+        for b, L in enumerate(w.lens):
+            n = need[b]
+            phys = perm[nxt:nxt + n]
+            nxt += n
+            table[b, :n] = phys.to(torch.int32)
+            # The sequence's rows, NaN from its length to the end of its last page.
+            rows = torch.full((w.H_kv, n * page_size, w.d), float("nan"), dtype=w.torch_dtype)
+            rows[:, :L] = src[b, :, :L]
+            pool[phys] = rows.reshape(w.H_kv, n, page_size, w.d).transpose(0, 1)
+        pools.append(pool.to(device))
+    return pools[0], pools[1], table.to(device)
 
 
 def make_prefill_paged(w: Workload, page_size: int, device="cpu", seed=None, spare_pages=3):
@@ -320,3 +325,24 @@ def sample_rows(S_q: int, n: int, seed: int, always=(0, 1, 63, 64, 127, 128)):
             out.append(r)
             seen.add(r)
     return sorted(out[:n])
+
+
+def sample_rows_per_block(S_q: int, n: int, seed: int, block: int = 32,
+                          always=(0, 1, 63, 64, 127, 128)):
+    """Seeded sample of ``n`` distinct query positions that holds one seeded
+    position in every ``block``-position block of ``[0, S_q)`` (so every
+    block of rows that one wave of a prefill workgroup owns is represented),
+    the listed tile-edge positions and the last row, filled up uniformly
+    without replacement."""
+    g = torch.Generator().manual_seed(seed)
+    nblk = (S_q + block - 1) // block
+    off = torch.randint(0, block, (nblk,), generator=g).tolist()
+    picked = {min(b * block + o, S_q - 1) for b, o in enumerate(off)}
+    picked |= {r for r in tuple(always) + (S_q - 1,) if 0 <= r < S_q}
+    if len(picked) > n:
+        raise ValueError(f"{len(picked)} required rows exceed the sample size {n}")
+    for r in torch.randperm(S_q, generator=g).tolist():
+        if len(picked) >= n:
+            break
+        picked.add(r)
+    return sorted(picked)

@@ -12,8 +12,6 @@ from gqa_flashattention_amd import inputs
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
-EDGE_ROWS = (0, 1, 63, 64, 127, 128, 4095, 8191)
-
 
 def _run(x, w, kv=None):
     o, lse = gq.prefill(x["q"], x["k"], x["v"], S_kv=w.S_kv, causal=w.causal,
@@ -22,49 +20,61 @@ def _run(x, w, kv=None):
     return o, lse
 
 
-def _pairs(w, n, seed):
-    """``n`` seeded (head, row) pairs spread over all heads, plus every edge
-    row on every head."""
-    rows = inputs.sample_rows(w.S_q, n, seed)
-    g = torch.Generator().manual_seed(seed + 1)
-    heads = torch.randperm(n, generator=g).remainder(w.H_q).tolist()
-    pairs = {(h, r) for h, r in zip(heads, rows)}
-    for r in EDGE_ROWS:
-        if r < w.S_q:
-            for h in range(w.H_q):
-                pairs.add((h, r))
-    by_head = {}
-    for h, r in sorted(pairs):
-        by_head.setdefault(h, []).append(r)
-    return by_head
+def _by_kv_head(w):
+    return [list(range(g * w.G, (g + 1) * w.G)) for g in range(w.H_kv)]
 
 
-def _check_sampled(x, w, o, lse, by_head, what):
-    q32, k32, v32 = np32(x["q"]), np32(x["k"]), np32(x["v"])
-    got, want, got_l, want_l = [], [], [], []
-    for h, rows in by_head.items():
-        rows = np.asarray(rows)
-        ro, rl = oracle.prefill(q32, k32, v32, w.S_kv, w.scale, causal=w.causal,
-                                causal_offset=w.offset, rows=rows, heads=[h])
-        got.append(np32(o[:, h, rows]).reshape(-1, w.d))
-        want.append(ro[:, 0].reshape(-1, w.d))
-        got_l.append(np32(lse[:, h, rows]).reshape(-1))
-        want_l.append(rl[:, 0].reshape(-1))
-    check_bf16(np.concatenate(got), np.concatenate(want), what)
-    check_lse(np.concatenate(got_l), np.concatenate(want_l), what, LSE_ATOL_BF16)
+@pytest.fixture(scope="module")
+def full_size_runs():
+    """One launch of each full-size prefill workload (the bench's launch);
+    inputs and results moved to the host once, shared by the per-KV-head
+    checks below."""
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache.clear()
+            w = inputs.WORKLOADS[name]
+            banner(name, "gqa_attn_prefill", f"S_q={w.S_q} S_kv={w.S_kv} offset={w.offset}")
+            x = inputs.make_prefill(w, device=DEV)
+            o, lse = _run(x, w)
+            assert torch.isfinite(o).all()
+            host = {n: np32(x[n]) for n in ("q", "k", "v")}
+            cache[name] = (w, host, np32(o), np32(lse))
+            del x, o, lse
+            torch.cuda.empty_cache()
+        return cache[name]
+    return get
 
 
-@pytest.mark.parametrize("name", ["prefill_causal_8k", "prefill_chunk_64k"])
-def test_prefill_workload_sampled(name):
-    """Full-size prefill (the bench's launch); oracle on 512 seeded (head, row)
-    pairs spanning all 64 heads plus the tile-edge rows of every head."""
-    w = inputs.WORKLOADS[name]
-    banner(name, "gqa_attn_prefill", f"S_q={w.S_q} S_kv={w.S_kv} offset={w.offset}")
-    x = inputs.make_prefill(w, device=DEV)
-    o, lse = _run(x, w)
-    assert torch.isfinite(o).all()
-    by_head = _pairs(w, 512, inputs.SEEDS[name])
-    _check_sampled(x, w, o, lse, by_head, name)
+@pytest.mark.parametrize("kvh", range(8))
+def test_prefill_causal_8k_every_element(full_size_runs, kvh):
+    """prefill_causal_8k checked on every element: all 8 192 rows of the 8
+    query heads of KV head ``kvh`` (O and LSE), so every workgroup of the
+    launch is compared with the oracle."""
+    w, x, o, lse = full_size_runs("prefill_causal_8k")
+    heads = _by_kv_head(w)[kvh]
+    ro, rl = oracle.prefill(x["q"], x["k"], x["v"], w.S_kv, w.scale, causal=w.causal,
+                            causal_offset=w.offset, heads=heads)
+    for i, h in enumerate(heads):
+        check_bf16(o[0, h], ro[0, i], f"prefill_causal_8k head {h}")
+    check_lse(lse[0, heads], rl[0], f"prefill_causal_8k KV head {kvh}", LSE_ATOL_BF16)
+
+
+@pytest.mark.parametrize("kvh", range(8))
+def test_prefill_chunk_64k_sampled_rows_all_heads(full_size_runs, kvh):
+    """prefill_chunk_64k on 512 seeded query positions, each for all 64
+    heads (the 8 heads of KV head ``kvh`` here): one position in every
+    32-position block (so every (KV head, position block) workgroup is
+    compared), the tile-edge positions and the last row."""
+    w, x, o, lse = full_size_runs("prefill_chunk_64k")
+    rows = np.asarray(inputs.sample_rows_per_block(w.S_q, 512, inputs.SEEDS[w.name]))
+    heads = _by_kv_head(w)[kvh]
+    ro, rl = oracle.prefill(x["q"], x["k"], x["v"], w.S_kv, w.scale, causal=w.causal,
+                            causal_offset=w.offset, rows=rows, heads=heads)
+    for i, h in enumerate(heads):
+        check_bf16(o[0, h][rows], ro[0, i], f"prefill_chunk_64k head {h}")
+    check_lse(lse[0, heads][:, rows], rl[0], f"prefill_chunk_64k KV head {kvh}", LSE_ATOL_BF16)
 
 
 SMALL = [
@@ -169,3 +179,74 @@ def test_prefill_max_jump_moves_reference(causal):
                             causal=causal, causal_offset=w.offset)
     check_bf16(np32(o[0]), ro[0], f"max jump causal={causal}")
     check_lse(np32(lse), rl, f"max jump causal={causal}", LSE_ATOL_BF16)
+
+
+def _plant_single_head_jumps(q, k, plants, q_row_dim=2):
+    """Make the scores of one query head jump far above its running
+    reference in one key tile, leaving the other heads of its KV head
+    nearly unaffected: the query head's component ``dim`` is set to 20 and
+    the keys of the tile get 30 in that component (about 53 natural-log
+    units, 76 in log2, above the rest of the row).  ``plants`` lists
+    (query head, KV head, first key, dim); ``q_row_dim`` is the axis of q
+    that holds the query heads' rows (q is [B, H_q, S_q, d] or
+    [total_q, H_q, d])."""
+    for h, kvh, k0, dim in plants:
+        if q_row_dim == 2:
+            q[:, h, :, dim] = 20.0
+        else:
+            q[:, h, dim] = 20.0
+        k[:, kvh, k0:k0 + 64, dim] = 30.0
+
+
+# (query head, its KV head, first key of the tile, component): tiles 4 and 6
+# are the first step of a group of two steps, where the fix-up used to read
+# a K ring slot that another wave may already be refilling; only one wave of
+# its workgroup takes the fix-up, so the waves drift apart.
+EVEN_TILE_JUMPS = ((3, 0, 256, 0), (12, 1, 384, 1))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_max_jump_even_tile_single_head(causal):
+    """One query head per KV head jumps on an even tile (the first step of a
+    step pair): every element against the oracle, O and LSE."""
+    w = inputs.Workload("t", "prefill", B=1, H_q=16, H_kv=2, d=128, dtype="bf16", S_q=200,
+                        S_kv=700, causal=causal, offset=500 if causal else 0)
+    banner("prefill_max_jump_even_tile", causal)
+    x = inputs.make_prefill(w, device=DEV, seed=25)
+    _plant_single_head_jumps(x["q"], x["k"], EVEN_TILE_JUMPS)
+    o, lse = _run(x, w)
+    ro, rl = oracle.prefill(np32(x["q"]), np32(x["k"]), np32(x["v"]), w.S_kv, w.scale,
+                            causal=causal, causal_offset=w.offset)
+    check_bf16(np32(o[0]), ro[0], f"even-tile jump causal={causal}")
+    check_lse(np32(lse), rl, f"even-tile jump causal={causal}", LSE_ATOL_BF16)
+    o2, lse2 = _run(x, w)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("page", [0, 16, 64])
+def test_prefill_varlen_and_paged_max_jump_even_tile(page):
+    """The same planted jumps in a varlen batch on a contiguous cache
+    (page = 0) and on paged caches: every element against the oracle, and
+    the paged launches bitwise equal to the contiguous one."""
+    q_lens, lens = (200, 77, 130), (700, 900, 130)
+    w = inputs.Workload("t", "prefill_paged" if page else "prefill_varlen", B=3, H_q=16,
+                        H_kv=2, d=128, dtype="bf16", q_lens=q_lens, lens=lens, kv_cap=960,
+                        causal=True, page_size=page)
+    banner("prefill_varlen_max_jump_even_tile", page)
+    x = inputs.make_prefill_varlen(w, device=DEV, seed=26)
+    _plant_single_head_jumps(x["q"], x["k"], EVEN_TILE_JUMPS, q_row_dim=1)
+    for b, L in enumerate(lens):     # padding stays NaN
+        x["k"][b, :, L:] = float("nan")
+    kw = dict(max_seqlen_q=max(q_lens), max_kv_len=max(lens), causal=True, scale=w.scale,
+              return_lse=True)
+    oc, lc = gq.prefill_varlen(x["q"], x["k"], x["v"], x["cu_seqlens_q"], x["kv_lens"], **kw)
+    torch.cuda.synchronize()
+    if page:
+        kp, vp, table = inputs.scatter_pages(w, x["k"], x["v"], page, 26, 3, DEV)
+        o, lse = gq.prefill_paged(x["q"], kp, vp, table, x["cu_seqlens_q"], x["kv_lens"], **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o, oc) and torch.equal(lse, lc)
+    ro, rl = oracle.prefill_varlen(np32(x["q"]), np32(x["k"]), np32(x["v"]),
+                                   np.array(x["cu_seqlens_q"].cpu()), np.array(lens), w.scale)
+    check_bf16(np32(oc), ro, f"varlen even-tile jump page={page}")
+    check_lse(np32(lc), rl, f"varlen even-tile jump page={page}", LSE_ATOL_BF16)
