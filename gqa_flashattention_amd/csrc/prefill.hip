@@ -623,12 +623,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // sits at offset 0), so the row addressing is recomputed here rather than
   // held in registers through the loop.
   int tid_e = threadIdx.x, bid_e = blockIdx.x;
-  const PrefillParams* pk =
-      reinterpret_cast<const PrefillParams*>(__builtin_amdgcn_kernarg_segment_ptr());
+  typedef const __attribute__((address_space(4))) PrefillParams KernargParams;
+  KernargParams* pk = (KernargParams*)__builtin_amdgcn_kernarg_segment_ptr();
   asm volatile("" : "+v"(tid_e), "+s"(bid_e), "+s"(pk));
+  const PrefillParams pa = *pk;   // scalar loads of the fields used below
   const int lane_e = tid_e & 63, c_e = tid_e & 31, h2_e = (tid_e >> 5) & 1;
   const int wave_e = __builtin_amdgcn_readfirstlane(tid_e >> 6);
-  const Place pe = locate(*pk, bid_e, wave_e);
+  const Place pe = locate(pa, bid_e, wave_e);
   const float lsum = lpart + __shfl_xor(lpart, 32, 64);
   const float inv = 1.f / lsum;
   char* stage = reinterpret_cast<char*>(&sK[0][0]) + wave_e * (32 * kD * 2);
@@ -643,7 +644,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     }
   {
     const int pc = lane_e & 15;
-    __bf16* obase = static_cast<__bf16*>(pk->o);
+    __bf16* obase = static_cast<__bf16*>(pa.o);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int r = 4 * k + (lane_e >> 4);
@@ -654,8 +655,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     }
   }
   const int qrow_e = pe.qw0 + c_e;
-  if (qrow_e < pe.S_q && pk->lse != nullptr && h2_e == 0)
-    pk->lse[pe.qrow0 + (size_t)qrow_e * pe.qstride] = (m_ref + __log2f(lsum)) * kLn2;
+  if (qrow_e < pe.S_q && pa.lse != nullptr && h2_e == 0)
+    pa.lse[pe.qrow0 + (size_t)qrow_e * pe.qstride] = (m_ref + __log2f(lsum)) * kLn2;
 }
 
 // Tile count of a varlen work item (b, pblk): the key tiles its workgroup
