@@ -51,14 +51,16 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, unsigned bytes) {
 // tell the addresses apart); the caller waits with s_waitcnt vmcnt before
 // the data is read.  Wait states inside the statement: the descriptor and
 // M0 value come from v_readfirstlane, and an LDS DMA may not directly
-// follow an M0 write.  M0 is declared clobbered, so the compiler keeps
-// nothing of its own there across the statement.
+// follow an M0 write.  M0 is a register the compiler reserves: it may
+// not be named as clobbered (that is undefined), and the compiler sets it
+// immediately before each of its own uses; a CPU test checks that the
+// built kernels write and read M0 nowhere but in these sequences.
 __device__ __forceinline__ void dma_load_x4(int voff, u32x4 rsrc, unsigned lds_dst) {
   const unsigned dst = __builtin_amdgcn_readfirstlane(lds_dst);
   asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(rsrc), "s"(dst)
-               : "memory", "m0");
+               : "memory");
 }
 
 // s_waitcnt immediate that waits until at most `n` (0..63) vector memory

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     int b, kvh, h, P0, qw0, S_q, S_kv, offset, qstride;
     size_t qrow0;
   };
-  auto locate = [&](const PrefillParams& p, int bid, int wave_u) -> Place {
+  auto locate = [&](const auto& p, int bid, int wave_u) -> Place {
     Place L;
     const int hpw = p.heads_per_wg;
     const int ngroups = p.G / hpw;
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   typedef const __attribute__((address_space(4))) PrefillParams KernargParams;
   KernargParams* pk = (KernargParams*)__builtin_amdgcn_kernarg_segment_ptr();
   asm volatile("" : "+v"(tid_e), "+s"(bid_e), "+s"(pk));
-  const PrefillParams pa = *pk;   // scalar loads of the fields used below
+  const auto& pa = *pk;   // fields read with scalar loads where used below
   const int lane_e = tid_e & 63, c_e = tid_e & 31, h2_e = (tid_e >> 5) & 1;
   const int wave_e = __builtin_amdgcn_readfirstlane(tid_e >> 6);
   const Place pe = locate(pa, bid_e, wave_e);

@@ -219,8 +219,11 @@ def test_prefill_max_jump_even_tile_single_head(causal):
                             causal=causal, causal_offset=w.offset)
     check_bf16(np32(o[0]), ro[0], f"even-tile jump causal={causal}")
     check_lse(np32(lse), rl, f"even-tile jump causal={causal}", LSE_ATOL_BF16)
-    o2, lse2 = _run(x, w)
-    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    # The waves of a workgroup drift apart here, so a cross-wave hazard
+    # shows as run-to-run differences: repeat and compare bit for bit.
+    for rep in range(8):
+        o2, lse2 = _run(x, w)
+        assert torch.equal(o, o2) and torch.equal(lse, lse2), f"repeat {rep} differs"
 
 
 @pytest.mark.parametrize("page", [0, 16, 64])
@@ -241,6 +244,10 @@ def test_prefill_varlen_and_paged_max_jump_even_tile(page):
               return_lse=True)
     oc, lc = gq.prefill_varlen(x["q"], x["k"], x["v"], x["cu_seqlens_q"], x["kv_lens"], **kw)
     torch.cuda.synchronize()
+    for rep in range(4):
+        o2, l2 = gq.prefill_varlen(x["q"], x["k"], x["v"], x["cu_seqlens_q"], x["kv_lens"], **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(oc, o2) and torch.equal(lc, l2), f"repeat {rep} differs"
     if page:
         kp, vp, table = inputs.scatter_pages(w, x["k"], x["v"], page, 26, 3, DEV)
         o, lse = gq.prefill_paged(x["q"], kp, vp, table, x["cu_seqlens_q"], x["kv_lens"], **kw)

@@ -37,3 +37,31 @@ def test_no_scratch(src, tmp_path):
     assert names and len(names) == len(scratch), "resource report not found"
     bad = [(n, sc) for n, sc in zip(names, scratch) if sc > ALLOWED_SCRATCH.get(n, 0)]
     assert not bad, f"kernels using scratch memory: {bad}"
+
+
+@pytest.mark.parametrize("src", [s for s in build.SOURCES if s != "api.hip"])
+def test_m0_only_in_lds_dma_sequences(src, tmp_path):
+    """M0 holds the LDS destination of the direct global -> LDS loads, which
+    are issued as inline assembly.  The compiler reserves M0 (it cannot be
+    declared clobbered), so check the generated code instead: every
+    instruction that names M0 is one of those sequences' `s_mov_b32 m0`,
+    followed (after at most one s_nop) by its `buffer_load ... lds`.  Any
+    other use would mean the compiler keeps a value of its own in M0 that
+    the sequence could overwrite."""
+    out = tmp_path / "out.s"
+    cmd = [build.hipcc(), *build.DEVICE_FLAGS, "-I", build.INCLUDE, "-I", build.CSRC,
+           "--cuda-device-only", "-S", os.path.join(build.CSRC, src), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln.split(";")[0].strip() for ln in out.read_text().splitlines()]
+    lines = [ln for ln in lines if ln and not ln.startswith((".", "//"))]
+    bad = []
+    for i, ln in enumerate(lines):
+        if not re.search(r"\bm0\b", ln):
+            continue
+        nxt = [x for x in lines[i + 1:i + 3] if x != "s_nop 0"]
+        ok = (re.fullmatch(r"s_mov_b32 m0, s\d+", ln) is not None and nxt
+              and re.match(r"buffer_load_dword\S* .* lds$", nxt[0]) is not None)
+        if not ok:
+            bad.append((i, ln))
+    assert not bad, f"M0 used outside the LDS DMA sequences: {bad[:5]}"
