@@ -21,7 +21,11 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
 STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
-                3: "GQA_ERR_WORKSPACE", 4: "GQA_ERR_HIP"}
+                3: "GQA_ERR_WORKSPACE", 4: "GQA_ERR_HIP", 5: "GQA_ERR_SCRATCH_LIMIT"}
+
+# Size of the fixed device scratch of gqa_attn_decode_noalloc
+# (GQA_DECODE_NOALLOC_SCRATCH_BYTES in the header).
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 # Every symbol include/gqa_attn.h declares, with its ctypes signature.
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -32,6 +36,8 @@ SIGNATURES = {
     "gqa_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "gqa_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                              _i, _vp, _sz, _vp]),
+    "gqa_attn_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                                     _i, _i, _vp]),
     "gqa_attn_decode_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
                                      _i, _i, _vp, _sz, _vp]),
     "gqa_attn_decode_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
@@ -211,6 +217,34 @@ def decode(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chunk_toke
                             workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, fn)
     return (out, lse) if return_lse else out
+
+
+def decode_noalloc(q, k_cache, v_cache, kv_lens, out, max_kv_len=None, scale=None,
+                   chunk_tokens=0, lse=None, stream=None):
+    """``gqa_attn_decode_noalloc`` on torch tensors: :func:`decode` without a
+    workspace (the library's fixed per-device scratch holds the partials)
+    and without allocating anything here either -- ``out`` (and ``lse``,
+    when the LSE is wanted) are the caller's.  Calls that overlap in time on
+    one device race on the shared scratch.  Returns ``out`` (and ``lse``
+    when given)."""
+    _require_gpu(q)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B, H_q, d], got shape {tuple(q.shape)}")
+    B, H_q, d = q.shape
+    dt = _dtype_code(q)
+    _check_kv(q, k_cache, v_cache, B)
+    _, H_kv, kv_cap, _ = k_cache.shape
+    _expect(kv_lens, "kv_lens", (B,), torch.int32, q.device)
+    _expect(out, "out", q.shape, q.dtype, q.device)
+    if lse is not None:
+        _expect(lse, "lse", (B, H_q), torch.float32, q.device)
+    max_kv_len = kv_cap if max_kv_len is None else int(max_kv_len)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib().gqa_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens),
+                                       _ptr(out), _ptr(lse), B, H_q, H_kv, d, kv_cap, max_kv_len,
+                                       scale, dt, chunk_tokens, _stream(stream))
+    _check(st, "gqa_attn_decode_noalloc")
+    return (out, lse) if lse is not None else out
 
 
 def decode_multi_split_tokens(B, H_q, H_kv, T_q, max_kv_len, chunk_tokens=0,

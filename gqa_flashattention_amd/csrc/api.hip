@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gqa_attn.h"
 #include "kernels.hpp"
 
@@ -133,11 +135,12 @@ const char* gqa_attn_status_string(int status) {
     case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
     case GQA_ERR_WORKSPACE: return "workspace missing or too small";
     case GQA_ERR_HIP: return "HIP runtime error at launch";
+    case GQA_ERR_SCRATCH_LIMIT: return "request exceeds the fixed scratch of the allocation-free decode";
     default: return "unknown status";
   }
 }
 
-int gqa_attn_version(void) { return 210; }
+int gqa_attn_version(void) { return 220; }
 
 int gqa_attn_decode_split_tokens(int B, int H_kv, int max_kv_len, int chunk_tokens, int dtype) {
   return split_tokens(B, H_kv, max_kv_len, chunk_tokens, dtype);
@@ -212,6 +215,65 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                     void* workspace, size_t workspace_bytes, void* stream) {
   return decode_phases(q, k_cache, v_cache, kv_lens, o, lse, B, H_q, H_kv, d, kv_cap, max_kv_len,
                        scale, dtype, chunk_tokens, workspace, workspace_bytes, stream,
+                       gqa::kDecodePartial | gqa::kDecodeCombine);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The allocation-free decode's partials: a fixed array in the library's
+// code object, one copy per device.  Host code never uses its name as an
+// address (that is a host-side stand-in); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept here.
+__device__ __align__(256) unsigned char scratch[GQA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(void* stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GQA_ERR_HIP;
+  if (dev >= kMaxDevices) return GQA_ERR_UNSUPPORTED;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+      return GQA_ERR_INVALID_ARG;
+    if (sdev != dev) return GQA_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return GQA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* kv_lens, void* o, float* lse, int B, int H_q,
+                            int H_kv, int d, int kv_cap, int max_kv_len, float scale, int dtype,
+                            int chunk_tokens, void* stream) {
+  // The size rule first (host arithmetic only), so that an oversized call
+  // is rejected before any device is touched; decode_phases checks the rest.
+  const size_t need =
+      gqa_attn_decode_workspace_bytes(B, H_q, H_kv, d, max_kv_len, chunk_tokens, dtype);
+  if (need > GQA_DECODE_NOALLOC_SCRATCH_BYTES) return GQA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int st = scratch_of_current_device(stream, &ws);
+    if (st != GQA_OK) return st;
+  }
+  return decode_phases(q, k_cache, v_cache, kv_lens, o, lse, B, H_q, H_kv, d, kv_cap, max_kv_len,
+                       scale, dtype, chunk_tokens, ws, GQA_DECODE_NOALLOC_SCRATCH_BYTES, stream,
                        gqa::kDecodePartial | gqa::kDecodeCombine);
 }
 

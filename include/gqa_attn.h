@@ -89,7 +89,9 @@ typedef enum {
   GQA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size or range  */
   GQA_ERR_UNSUPPORTED = 2,  /* valid request the library does not implement */
   GQA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required  */
-  GQA_ERR_HIP = 4           /* the HIP runtime rejected a launch           */
+  GQA_ERR_HIP = 4,          /* the HIP runtime rejected a launch           */
+  GQA_ERR_SCRATCH_LIMIT = 5 /* gqa_attn_decode_noalloc: the call needs more
+                               than its fixed device scratch               */
 } gqa_status_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -153,6 +155,36 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                     int B, int H_q, int H_kv, int d, int kv_cap,
                     int max_kv_len, float scale, int dtype, int chunk_tokens,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_attn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, the same kernels and the same
+ * results bit for bit.  The split partials live in a fixed device array of
+ * GQA_DECODE_NOALLOC_SCRATCH_BYTES bytes that the library's code object
+ * holds on every device it is loaded on, until the process ends; its device
+ * address is looked up once per device, on the first call made with that
+ * device current (hipGetSymbolAddress, no allocation).  Nothing in it needs
+ * to start at zero: every partial is written before it is read.
+ *
+ *  - `stream` must belong to the current device (else GQA_ERR_INVALID_ARG).
+ *  - A call whose partials would need more than the scratch
+ *    (gqa_attn_decode_workspace_bytes(...) > GQA_DECODE_NOALLOC_SCRATCH_BYTES)
+ *    returns GQA_ERR_SCRATCH_LIMIT before launching anything.  The limit
+ *    holds, for example, B = 4 sequences of up to 131072 keys at H_q = 64
+ *    with the automatic split.
+ *  - All calls on one device share its scratch: calls that overlap in time
+ *    on one device (two streams, or two host threads) race and give wrong
+ *    results.  Serialise them.
+ *  - It calls no hipMalloc, hipFree or other allocating routine.
+ */
+#define GQA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int gqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* kv_lens, void* o, float* lse,
+                            int B, int H_q, int H_kv, int d, int kv_cap,
+                            int max_kv_len, float scale, int dtype, int chunk_tokens,
+                            void* stream);
 
 /*
  * The two launches of gqa_attn_decode, separately: _partial runs the split

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = binding.lib()
-    for s in range(5):
+    for s in range(6):
         assert L.gqa_attn_status_string(s)
     assert L.gqa_attn_status_string(99) == b"unknown status"
     assert L.gqa_attn_version() >= 100
@@ -337,3 +337,19 @@ def test_paged_split_rules():
     assert L.gqa_attn_decode_paged_split_tokens(1, 64, 8, 4, 16, 131072, 0, BF16) == 1920
     assert L.gqa_attn_decode_paged_split_tokens(1, 64, 8, 4, 16, 131072, 2048, BF16) == -INVALID
     assert L.gqa_attn_decode_paged_split_tokens(1, 64, 8, 4, 24, 131072, 0, BF16) == -INVALID
+
+
+def test_decode_noalloc_rejects_oversized_before_any_device_call():
+    """The allocation-free decode refuses a call whose partials exceed its
+    fixed scratch with GQA_ERR_SCRATCH_LIMIT, from host arithmetic alone
+    (no device is touched: this runs without a GPU)."""
+    L = binding.lib()
+    SCRATCH_LIMIT = 5
+    need = L.gqa_attn_decode_workspace_bytes(8, 64, 8, 128, 131072, 0, BF16)
+    assert need > binding.DECODE_NOALLOC_SCRATCH_BYTES
+    st = L.gqa_attn_decode_noalloc(P, P, P, P, P2, None, 8, 64, 8, 128, 131072, 131072,
+                                   0.088, BF16, 0, None)
+    assert st == SCRATCH_LIMIT
+    # The workloads it is sized for fit: four 128K-key sequences.
+    assert L.gqa_attn_decode_workspace_bytes(4, 64, 8, 128, 131072, 0, BF16) <= \
+        binding.DECODE_NOALLOC_SCRATCH_BYTES
