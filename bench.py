@@ -19,6 +19,14 @@ decode calls and K split-kernel launches that follow; warm-up calls are
 untimed.  ``cpu_baseline`` times the fp64 oracle on the host cores on a
 bounded sample of the same workload.
 
+After the headline steps, the default run also times the other three
+measured workloads -- decode_small_f32 (latency bound), decode_ragged_b4
+(HBM bound) and prefill_chunk_64k (matrix-core bound) -- each with its own
+roofline object (median and mean), in ``configs``; and a plain device copy
+of 1 GiB (``copy_ceiling``: read + write bytes over its median time), the
+streaming rate this GPU reaches outside the library, as context for the
+spec peak the fractions use.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 
@@ -59,6 +67,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of each oracle sample")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other measured workloads and the copy ceiling after the "
+                         "headline steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (calibrates the HBM "
                          "byte counters under rocprofv3 --pmc)")
@@ -99,6 +110,167 @@ def traffic_from_profiles(kernel: str, workload: str):
     if sha != ent.get("source_sha256_16"):
         return None
     return ent["bytes_per_launch"]
+
+
+TRAFFIC_SOURCE = ("profiles/all_workloads_kernel_stats_and_counters.md: calibrated rocprofv3 "
+                  "FETCH_SIZE + WRITE_SIZE per launch, used only when that table was taken on the "
+                  "kernel's current source (sha256 match); otherwise null")
+
+
+def measure_copy_ceiling(reps=20):
+    """Median time of a plain 1 GiB device-to-device copy (torch copy_):
+    (read + write bytes) / time, in GB/s."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    med = ms[len(ms) // 2]
+    del dst
+    # Read-only streaming: a float32 sum over the same 1 GiB.
+    x = src.view(torch.float32)
+    for _ in range(3):
+        x.sum()
+    for a, b in ev:
+        a.record(stream)
+        x.sum()
+        b.record(stream)
+    torch.cuda.synchronize()
+    rs = sorted(a.elapsed_time(b) for a, b in ev)
+    rmed = rs[len(rs) // 2]
+    del src, x
+    torch.cuda.empty_cache()
+    return {"GB_s": round(2 * n / (med * 1e-3) / 1e9, 1), "bytes_read": n, "bytes_written": n,
+            "ms_median": round(med, 4), "reps": reps,
+            "kind": "torch device-to-device copy of 1 GiB (read + write bytes / median time)",
+            "read_only_GB_s": round(n / (rmed * 1e-3) / 1e9, 1),
+            "read_only_kind": "torch float32 sum over the same 1 GiB (bytes read / median time)"}
+
+
+def _stats(ms_list):
+    a = sorted(ms_list)
+    return sum(a) / len(a), a[len(a) // 2]
+
+
+def time_decode_workload(name, steps, warmup):
+    """Decode workload `name` (gqa_attn_decode): per-call events (median and
+    mean), back-to-back calls, and the split kernel alone back to back.
+    Caches smaller than 512 MiB rotate over 4 copies (the Infinity Cache
+    holds 256 MB)."""
+    import torch
+    from gqa_flashattention_amd import binding as gq
+    from gqa_flashattention_amd import inputs
+    w = inputs.WORKLOADS[name]
+    dt = gq.DTYPE_F32 if w.dtype == "f32" else gq.DTYPE_BF16
+    ncopies = 4 if w.kv_bytes() < (512 << 20) else 1
+    copies = [inputs.make_decode(w, device="cuda:0", seed=inputs.SEEDS[name] + 100 * i)
+              for i in range(ncopies)]
+    ws = torch.empty(gq.decode_workspace_bytes(w.B, w.H_q, w.H_kv, w.d, w.max_kv_len, 0, dt),
+                     dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(copies[0]["q"])
+    stream = torch.cuda.current_stream()
+
+    def call(i, phase="both"):
+        x = copies[i % ncopies]
+        gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=w.max_kv_len, scale=w.scale,
+                  out=out, workspace=ws, stream=stream, phase=phase)
+
+    for i in range(warmup):
+        call(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        call(i)
+        b.record(stream)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record(stream)
+    for i in range(steps):
+        call(i)
+    e[1].record(stream)
+    e[2].record(stream)
+    for i in range(steps):
+        call(i, "partial")
+    e[3].record(stream)
+    torch.cuda.synchronize()
+    mean_ms, med_ms = _stats([a.elapsed_time(b) for a, b in ev])
+    b2b_us = e[0].elapsed_time(e[1]) * 1e3 / steps
+    part_us = e[2].elapsed_time(e[3]) * 1e3 / steps
+    gbs = w.decode_bytes() / (b2b_us * 1e-6) / 1e9
+    part_bytes = w.kv_bytes() + w.B * w.H_q * w.T_q * w.d * w.elem_bytes
+    part_gbs = part_bytes / (part_us * 1e-6) / 1e9
+    res = {"entry_point": "gqa_attn_decode", "B": w.B, "kv_lens": list(w.lens), "dtype": w.dtype,
+           "kv_copies": ncopies, "keys_per_split": gq.decode_split_tokens(w.B, w.H_kv,
+                                                                        w.max_kv_len, 0, dt),
+           "us_per_call_back_to_back": round(b2b_us, 3),
+           "us_per_call_median": round(med_ms * 1e3, 3), "us_per_call_mean": round(mean_ms * 1e3, 3),
+           "bytes_per_call": w.decode_bytes(), "GB_s": round(gbs, 2),
+           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "roofline": {"bound": "hbm" if w.dtype == "bf16" else "latency",
+                        "kernel": f"decode_partial_{w.dtype}_kernel",
+                        "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(part_gbs / HBM_PEAK_GBS, 4),
+                        "traffic": traffic_from_profiles("decode_partial", name),
+                        "traffic_source": TRAFFIC_SOURCE,
+                        "algorithmic_bytes_per_launch": part_bytes,
+                        "launch_us_mean": round(part_us, 3)}}
+    del copies, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_prefill_workload(name, steps, warmup):
+    """Prefill workload `name` (gqa_attn_prefill): per-call events, TFLOP/s
+    of the median and of the mean call."""
+    import torch
+    from gqa_flashattention_amd import binding as gq
+    from gqa_flashattention_amd import inputs
+    w = inputs.WORKLOADS[name]
+    x = inputs.make_prefill(w, device="cuda:0")
+    out = torch.empty_like(x["q"])
+    stream = torch.cuda.current_stream()
+
+    def call():
+        gq.prefill(x["q"], x["k"], x["v"], S_kv=w.S_kv, causal=w.causal, causal_offset=w.offset,
+                   scale=w.scale, out=out, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    mean_ms, med_ms = _stats([a.elapsed_time(b) for a, b in ev])
+    tf_med = w.prefill_flops() / (med_ms * 1e-3) / 1e12
+    tf_mean = w.prefill_flops() / (mean_ms * 1e-3) / 1e12
+    res = {"entry_point": "gqa_attn_prefill", "S_q": w.S_q, "S_kv": w.S_kv, "offset": w.offset,
+           "causal": w.causal, "ms_median": round(med_ms, 6), "ms_mean": round(mean_ms, 6),
+           "flops_per_call": w.prefill_flops(), "TFLOP_s": round(tf_med, 2),
+           "TFLOP_s_mean": round(tf_mean, 2),
+           "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<false, false>",
+                        "achieved": round(tf_med, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf_med / BF16_PEAK_TFLOPS, 4),
+                        "frac_mean": round(tf_mean / BF16_PEAK_TFLOPS, 4),
+                        "traffic": traffic_from_profiles("prefill", name),
+                        "traffic_source": TRAFFIC_SOURCE,
+                        "launch_us_median": round(med_ms * 1e3, 3),
+                        "launch_us_mean": round(mean_ms * 1e3, 3)}}
+    del x, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_threads():
@@ -385,6 +557,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(mean(step_ms), 6),
+        "ms_per_step_median": round(median(step_ms), 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -434,12 +607,15 @@ def main():
                            "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(part_gbs / HBM_PEAK_GBS, 4),
                            "traffic": traffic_from_profiles(tkey, wd.name),
+                           "traffic_source": TRAFFIC_SOURCE,
                            "algorithmic_bytes_per_launch": part_bytes,
                            "launch_us_mean": round(part_us, 3)}
     if do_pre:
-        t_s = mean(pre_ms) / 1e3
-        tf = wp.prefill_flops() / t_s / 1e12
+        # The median call is the reported figure; the mean is given beside it.
+        tf = wp.prefill_flops() / (median(pre_ms) / 1e3) / 1e12
+        tf_mean = wp.prefill_flops() / (mean(pre_ms) / 1e3) / 1e12
         out["prefill"] = {"value": round(tf, 2), "unit": "TFLOP/s",
+                          "value_of_mean_call": round(tf_mean, 2),
                           "ms_mean": round(mean(pre_ms), 6), "ms_median": round(median(pre_ms), 6),
                           "flops_per_call": wp.prefill_flops(),
                           "roofline": {"bound": "mfma",
@@ -447,13 +623,35 @@ def main():
                                                  f"{str(paged_pre).lower()}>",
                                        "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                       "frac_mean": round(tf_mean / BF16_PEAK_TFLOPS, 4),
                                        "traffic": traffic_from_profiles("prefill", wp.name),
+                                       "traffic_source": TRAFFIC_SOURCE,
+                                       "launch_us_median": round(median(pre_ms) * 1e3, 3),
                                        "launch_us_mean": round(mean(pre_ms) * 1e3, 3)}}
 
     if not do_dec:   # prefill-only run: its throughput is the value
         out["value"] = out["prefill"]["value"]
         out["unit"] = "TFLOP/s"
         out["roofline"] = out["prefill"]["roofline"]
+
+    # The other measured workloads and the copy ceiling, after the headline
+    # (default run only: the headline workloads and both entry points).
+    default_run = (args.only == "both" and args.decode_workload == "decode_llama70b_32k"
+                   and args.prefill_workload == "prefill_causal_8k" and args.chunk == 0)
+    if default_run and not args.no_extra:
+        del copies, ws, xp, o_dec, o_pre
+        torch.cuda.empty_cache()
+        cfg = {}
+        for name in ("decode_small_f32", "decode_ragged_b4"):
+            cfg[name] = time_decode_workload(name, K, max(args.warmup, 10))
+        cfg["prefill_chunk_64k"] = time_prefill_workload("prefill_chunk_64k", min(K, 20),
+                                                         min(max(args.warmup // 10, 3), 10))
+        out["configs"] = cfg
+        out["copy_ceiling"] = measure_copy_ceiling()
+        if not args.no_cpu_baseline:
+            # Re-create the headline inputs for the oracle leg (same seeds).
+            copies = [inputs.make_decode(wd, device=dev, seed=inputs.SEEDS[wd.name])]
+            xp = inputs.make_prefill(wp, device=dev)
 
     if not args.no_cpu_baseline:
         import numpy as np  # noqa: F401
