@@ -175,7 +175,8 @@ def time_decode_workload(name, steps, warmup):
     ncopies = 4 if w.kv_bytes() < (512 << 20) else 1
     copies = [inputs.make_decode(w, device="cuda:0", seed=inputs.SEEDS[name] + 100 * i)
               for i in range(ncopies)]
-    ws = torch.empty(gq.decode_workspace_bytes(w.B, w.H_q, w.H_kv, w.d, w.max_kv_len, 0, dt),
+    # Zero-filled: the fused form's arrival counters start at zero.
+    ws = torch.zeros(gq.decode_workspace_bytes(w.B, w.H_q, w.H_kv, w.d, w.max_kv_len, 0, dt),
                      dtype=torch.uint8, device="cuda:0")
     out = torch.empty_like(copies[0]["q"])
     stream = torch.cuda.current_stream()
@@ -193,7 +194,9 @@ def time_decode_workload(name, steps, warmup):
         a.record(stream)
         call(i)
         b.record(stream)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for i in range(warmup):
+        call(i, "fused")
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     e[0].record(stream)
     for i in range(steps):
         call(i)
@@ -202,10 +205,15 @@ def time_decode_workload(name, steps, warmup):
     for i in range(steps):
         call(i, "partial")
     e[3].record(stream)
+    e[4].record(stream)
+    for i in range(steps):
+        call(i, "fused")
+    e[5].record(stream)
     torch.cuda.synchronize()
     mean_ms, med_ms = _stats([a.elapsed_time(b) for a, b in ev])
     b2b_us = e[0].elapsed_time(e[1]) * 1e3 / steps
     part_us = e[2].elapsed_time(e[3]) * 1e3 / steps
+    fused_us = e[4].elapsed_time(e[5]) * 1e3 / steps
     gbs = w.decode_bytes() / (b2b_us * 1e-6) / 1e9
     part_bytes = w.kv_bytes() + w.B * w.H_q * w.T_q * w.d * w.elem_bytes
     part_gbs = part_bytes / (part_us * 1e-6) / 1e9
@@ -216,6 +224,9 @@ def time_decode_workload(name, steps, warmup):
            "us_per_call_median": round(med_ms * 1e3, 3), "us_per_call_mean": round(mean_ms * 1e3, 3),
            "bytes_per_call": w.decode_bytes(), "GB_s": round(gbs, 2),
            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "fused": {"entry_point": "gqa_attn_decode_fused",
+                     "us_per_call_back_to_back": round(fused_us, 3),
+                     "GB_s": round(w.decode_bytes() / (fused_us * 1e-6) / 1e9, 2)},
            "roofline": {"bound": "hbm" if w.dtype == "bf16" else "latency",
                         "kernel": f"decode_partial_{w.dtype}_kernel",
                         "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -462,7 +473,7 @@ def main():
             need = gq.decode_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.max_kv_len,
                                              args.chunk, dec_dtype)
             chunk = gq.decode_split_tokens(wd.B, wd.H_kv, wd.max_kv_len, args.chunk, dec_dtype)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev)   # fused counters start at zero
         o_dec = torch.empty_like(copies[0]["q"])
     if do_pre:
         if paged_pre:
@@ -520,6 +531,11 @@ def main():
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     kd = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     kp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    kf = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    fused_ok = do_dec and not multi and not paged
+    if fused_ok:
+        for i in range(min(args.warmup, 20)):
+            decode_call(i, "fused")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(K):
@@ -539,6 +555,11 @@ def main():
         for i in range(K):
             decode_call(i, "partial")
         kp[1].record(stream)
+        if fused_ok:
+            kf[0].record(stream)
+            for i in range(K):
+                decode_call(i, "fused")
+            kf[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
@@ -593,6 +614,11 @@ def main():
                          "GB_s": round(gbs, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                          "bytes_per_call": wd.decode_bytes(),
                          "partial_kernel_us_mean": round(part_us, 3)}
+        if fused_ok:
+            f_us = kf[0].elapsed_time(kf[1]) * 1e3 / K
+            out["decode"]["fused"] = {"entry_point": "gqa_attn_decode_fused",
+                                      "us_per_call_back_to_back": round(f_us, 3),
+                                      "GB_s": round(wd.decode_bytes() / (f_us * 1e-6) / 1e9, 2)}
         if multi and wd.G * wd.T_q > 16:
             rows = wd.G * wd.T_q
             rgroups = 1 if rows <= 32 else (2 if rows <= 64 else 4)

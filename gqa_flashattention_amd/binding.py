@@ -36,6 +36,8 @@ SIGNATURES = {
     "gqa_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "gqa_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                              _i, _vp, _sz, _vp]),
+    "gqa_attn_decode_fused": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
+                                   _i, _vp, _sz, _vp]),
     "gqa_attn_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
                                      _i, _i, _vp]),
     "gqa_attn_decode_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
@@ -186,7 +188,9 @@ def decode(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chunk_toke
     fp32), kv_lens ``[B]`` int32 on the device.  ``max_kv_len`` defaults to
     ``kv_cap``.  ``phase`` = "partial" or "combine" issues only that launch
     (``gqa_attn_decode_partial`` / ``_combine``; pass the same ``workspace``
-    to both).  Returns ``o`` (and ``lse`` when ``return_lse``).
+    to both); "fused" runs ``gqa_attn_decode_fused`` (one launch; a
+    caller-supplied workspace must have been zero-filled before its first
+    fused call).  Returns ``o`` (and ``lse`` when ``return_lse``).
     """
     _require_gpu(q)
     if q.dim() != 3:
@@ -207,10 +211,12 @@ def decode(q, k_cache, v_cache, kv_lens, max_kv_len=None, scale=None, chunk_toke
         _expect(lse, "lse", (B, H_q), torch.float32, q.device)
     need = decode_workspace_bytes(B, H_q, H_kv, d, max_kv_len, chunk_tokens, dt)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zeros: the fused form's arrival counters must start at zero (every
+        # fused call leaves them zero); the other phases ignore them.
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     _expect_workspace(workspace, q.device, need)
     fn = {"both": "gqa_attn_decode", "partial": "gqa_attn_decode_partial",
-          "combine": "gqa_attn_decode_combine"}[phase]
+          "combine": "gqa_attn_decode_combine", "fused": "gqa_attn_decode_fused"}[phase]
     st = getattr(lib(), fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens), _ptr(out),
                             _ptr(lse) if return_lse else None, B, H_q, H_kv, d, kv_cap,
                             max_kv_len, scale, dt, chunk_tokens, _ptr(workspace),

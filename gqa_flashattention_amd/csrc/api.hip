@@ -112,14 +112,23 @@ int paged_split_tokens(int B, int H_q, int H_kv, int T_q, int page_size, int max
   return c;
 }
 
-// Workspace: [partial O] [partial (m, l)], each region 256-byte aligned.
+// Decode workspace: [arrival counters, a fixed 64 KiB] [partial O]
+// [partial (m, l)], each region 256-byte aligned.  The counters (one uint32
+// per (sequence, KV head), at most kMaxCounters) are written only by the
+// fused decode, which leaves them zero; they sit at the same offset for
+// every shape, so a workspace zeroed once serves fused calls of any shape
+// while partials of any call never land on them.
+constexpr size_t kCounterBytes = 64 << 10;
+constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(unsigned));
+
 struct WsLayout {
-  size_t ml_off, total;
+  size_t o_off, ml_off, total;
 };
 
 WsLayout ws_layout(int B, int H_q, int n_split) {
   WsLayout w;
-  w.ml_off = round_up((size_t)B * H_q * n_split * kD * sizeof(float), kWsAlign);
+  w.o_off = kCounterBytes;
+  w.ml_off = w.o_off + round_up((size_t)B * H_q * n_split * kD * sizeof(float), kWsAlign);
   w.total = w.ml_off + round_up((size_t)B * H_q * n_split * 2 * sizeof(float), kWsAlign);
   return w;
 }
@@ -173,6 +182,7 @@ static int decode_phases(const void* q, const void* k_cache, const void* v_cache
   if (chunk_tokens < 0) return GQA_ERR_INVALID_ARG;
   if (B > 65535 || H_kv > 65535) return GQA_ERR_INVALID_ARG;
   if (d != kD || H_q / H_kv > kMaxG) return GQA_ERR_UNSUPPORTED;
+  if ((phases & gqa::kDecodeFused) && (long long)B * H_kv > kMaxCounters) return GQA_ERR_UNSUPPORTED;
   const int chunk = split_tokens(B, H_kv, max_kv_len, chunk_tokens, dtype);
   if (chunk <= 0) return GQA_ERR_INVALID_ARG;
   const int n_split = (max_kv_len + chunk - 1) / chunk;
@@ -187,8 +197,9 @@ static int decode_phases(const void* q, const void* k_cache, const void* v_cache
   p.kv_lens = kv_lens;
   p.o = o;
   p.lse = lse;
-  p.ws_o = static_cast<float*>(workspace);
+  p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+  p.counters = (phases & gqa::kDecodeFused) ? static_cast<unsigned*>(workspace) : nullptr;
   p.B = B;
   p.H_q = H_q;
   p.H_kv = H_kv;
@@ -277,6 +288,16 @@ int gqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_ca
                        gqa::kDecodePartial | gqa::kDecodeCombine);
 }
 
+int gqa_attn_decode_fused(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
+                          int d, int kv_cap, int max_kv_len, float scale, int dtype,
+                          int chunk_tokens, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return decode_phases(q, k_cache, v_cache, kv_lens, o, lse, B, H_q, H_kv, d, kv_cap, max_kv_len,
+                       scale, dtype, chunk_tokens, workspace, workspace_bytes, stream,
+                       gqa::kDecodePartial | gqa::kDecodeFused);
+}
+
 int gqa_attn_decode_partial(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* kv_lens, void* o, float* lse, int B, int H_q,
                             int H_kv, int d, int kv_cap, int max_kv_len, float scale, int dtype,
@@ -346,8 +367,9 @@ static int decode_multi_phases(const void* q, const void* k_cache, const void* v
   p.kv_lens = kv_lens;
   p.o = o;
   p.lse = lse;
-  p.ws_o = static_cast<float*>(workspace);
+  p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+  p.counters = nullptr;
   p.B = B;
   p.H_q = H_q;
   p.H_kv = H_kv;
@@ -461,8 +483,9 @@ static int decode_paged_phases(const void* q, const void* k_pages, const void* v
   p.kv_lens = kv_lens;
   p.o = o;
   p.lse = lse;
-  p.ws_o = static_cast<float*>(workspace);
+  p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+  p.counters = nullptr;
   p.B = B;
   p.H_q = H_q;
   p.H_kv = H_kv;

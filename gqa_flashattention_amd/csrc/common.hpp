@@ -42,6 +42,12 @@ __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned int, b);
 }
 
+// s_waitcnt immediate that waits until at most `n` (0..63) vector memory
+// operations of this wave are outstanding (lgkm and exp counters ignored).
+constexpr unsigned vmcnt_imm(int n) {
+  return 0x0F70u | ((unsigned)n & 15u) | (((unsigned)n >> 4) << 14);
+}
+
 __device__ __forceinline__ float wave_max_xor(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, 64));
 }

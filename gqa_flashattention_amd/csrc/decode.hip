@@ -27,6 +27,8 @@
 // costs either an L2 write-back per workgroup or agent-coherent accesses,
 // and the merge then runs serially on one CU at the end.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -172,6 +174,232 @@ __device__ __forceinline__ void fold_block(State& st, const Block& blk, const bf
   }
 }
 
+// Online log-sum-exp merge of split partials, NG at a time per lane so that
+// all of a group's loads are in flight together.  (M, acc, lacc) is the running
+// state; a group is folded in with the merge rule of §4: rescale both sides
+// to the larger max and add.
+struct MergeAcc {
+  float M;
+  f32x4 acc;
+  float lacc;
+};
+
+constexpr int kCombSlots = 8;     // split slots per wave (lane / 8)
+
+template <int NG>   // splits per lane and load round
+struct MergeLoads {
+  float m[NG], l[NG];
+  f32x4 o[NG];
+};
+
+// Loads splits s0, s0 + stride, ...; indices at or past `s_alloc` (the
+// partials the workspace holds per row) re-read the last one, so every load
+// is unconditional and all of them are in flight together.  Such splits lie
+// past the sequence's split count and are discarded by merge_fold.
+template <int NG>
+__device__ __forceinline__ void merge_load(MergeLoads<NG>& g, const float* ml, const float* po, int s0,
+                                           int s_alloc, int stride) {
+#pragma unroll
+  for (int u = 0; u < NG; ++u) {
+    const int s = min(s0 + u * stride, s_alloc - 1);
+    const f32x2 m2 = *reinterpret_cast<const f32x2*>(ml + 2 * s);
+    g.o[u] = *reinterpret_cast<const f32x4*>(po + (size_t)s * kD);
+    g.m[u] = m2[0];
+    g.l[u] = m2[1];
+  }
+}
+
+// Merges (m, acc, l) into `st` with the rule of §4.  Branch-free: with both
+// sides empty (m = -inf) the reference is 0 and both weights are 0.
+__device__ __forceinline__ void merge_pair(MergeAcc& st, float m, f32x4 acc, float l) {
+  const float gm = fmaxf(st.M, m);
+  const float ref = gm == kNegInf ? 0.f : gm;
+  const float c0 = fast_exp2(st.M - ref);
+  const float c1 = fast_exp2(m - ref);
+  st.acc = st.acc * c0 + acc * c1;
+  st.lacc = st.lacc * c0 + l * c1;
+  st.M = gm;
+}
+
+// Folds the loaded splits below `s_valid` (the splits of this call) into
+// `st`; the others are replaced by the identity (-inf, 0, 0) before use.
+template <int NG>
+__device__ __forceinline__ void merge_fold(MergeAcc& st, MergeLoads<NG>& g, int s0, int s_valid,
+                                           int stride) {
+#pragma unroll
+  for (int u = 0; u < NG; ++u) {
+    if (s0 + u * stride >= s_valid) {
+      g.m[u] = kNegInf;
+      g.l[u] = 0.f;
+      g.o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  float gm = st.M;
+#pragma unroll
+  for (int u = 0; u < NG; ++u) gm = fmaxf(gm, g.m[u]);
+  // Branch-free (so that no load is sunk behind a branch): with every side
+  // empty, gm = -inf and the weights below are exp2(-inf) = 0.
+  const float ref = gm == kNegInf ? 0.f : gm;
+  const float c = fast_exp2(st.M - ref);
+  st.acc *= c;
+  st.lacc *= c;
+#pragma unroll
+  for (int u = 0; u < NG; ++u) {
+    const float w = fast_exp2(g.m[u] - ref);
+    st.acc += w * g.o[u];
+    st.lacc += w * g.l[u];
+  }
+  st.M = gm;
+}
+
+// Combine: one wave per (output row, quarter of d), rows being (sequence,
+// query head, token); the 4 waves of a row run on different CUs, so a row's
+// partials are fetched by four load pipelines at once.  Lane l takes split
+// slot j = l / 8 (splits j, j + 8, j + 16, ...) and output columns
+// 32*quarter + 4*(l % 8) .. +4; the 8 slots then merge across lanes
+// (xor 8, 16, 32).  Normalises once and rounds to the output dtype (the
+// final O / l of §4).  The first 8*NG splits' loads are issued together with
+// the sequence length's, so a call of up to 8*NG splits costs one memory
+// round trip; splits past the sequence's count are discarded after the
+// loads.  NG (2, 4 or 8) follows the workspace's split count, so that a row
+// with few splits does not load the same partial several times.
+template <typename OutT, int NG, int U>
+__device__ __forceinline__ void combine_rows(const DecodeParams& p, const int (&bh)[U],
+                                             const int (&quarter)[U], int count, int lane) {
+  // U (row, quarter) units, count of them valid: the first load round of
+  // every unit is issued before any is folded, so the units share one
+  // memory round trip; each unit's arithmetic is the same sequence as
+  // with U = 1.
+  const int slot = lane >> 3;
+  MergeLoads<NG> g[U];
+  int len[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u < count) {
+      const size_t part0 = (size_t)bh[u] * p.n_split_max;
+      len[u] = p.kv_lens[bh[u] / (p.H_q * p.T_q)];
+      merge_load(g[u], p.ws_ml + 2 * part0, p.ws_o + part0 * kD + 32 * quarter[u] + 4 * (lane & 7),
+                 slot, p.n_split_max, kCombSlots);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u >= count) break;
+    const int d0 = 32 * quarter[u] + 4 * (lane & 7);
+    const size_t part0 = (size_t)bh[u] * p.n_split_max;
+    const float* ml = p.ws_ml + 2 * part0;
+    const float* po = p.ws_o + part0 * kD + d0;
+    const int L = min(len[u], p.max_kv_len);
+    const int ns = (L + p.chunk - 1) / p.chunk;
+    MergeAcc st{kNegInf, {0.f, 0.f, 0.f, 0.f}, 0.f};
+    merge_fold(st, g[u], slot, ns, kCombSlots);
+    for (int s0 = slot + kCombSlots * NG; s0 < ns; s0 += kCombSlots * NG) {
+      merge_load(g[u], ml, po, s0, p.n_split_max, kCombSlots);
+      merge_fold(st, g[u], s0, ns, kCombSlots);
+    }
+#pragma unroll
+    for (int mask = 8; mask < 64; mask <<= 1) {
+      f32x4 ao;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ao[i] = __shfl_xor(st.acc[i], mask, 64);
+      const float mo = __shfl_xor(st.M, mask, 64);
+      const float lo = __shfl_xor(st.lacc, mask, 64);
+      merge_pair(st, mo, ao, lo);
+    }
+    if (slot == 0) {
+      const float inv = 1.f / st.lacc;
+      OutT* o = static_cast<OutT*>(p.o) + (size_t)bh[u] * kD + d0;
+      if constexpr (sizeof(OutT) == 2) {
+        const u32x2 w = {pack_bf16x2(st.acc[0] * inv, st.acc[1] * inv),
+                         pack_bf16x2(st.acc[2] * inv, st.acc[3] * inv)};
+        *reinterpret_cast<u32x2*>(o) = w;
+      } else {
+        *reinterpret_cast<f32x4*>(o) = st.acc * inv;
+      }
+      if (p.lse != nullptr && lane == 0 && quarter[u] == 0)
+        p.lse[bh[u]] = (st.M + __log2f(st.lacc)) * kLn2;
+    }
+  }
+}
+
+template <typename OutT, int NG>
+__device__ __forceinline__ void combine_row(const DecodeParams& p, int bh, int quarter, int lane) {
+  const int bhs[1] = {bh}, qs[1] = {quarter};
+  combine_rows<OutT, NG, 1>(p, bhs, qs, 1, lane);
+}
+
+// Splits per lane and load round of the merge for a workspace of
+// `n_split_max` partials per row (the combine launch uses the same rule).
+__host__ __device__ constexpr int combine_ng(int n_split_max) {
+  return n_split_max <= 16 ? 2 : n_split_max <= 32 ? 4 : 8;
+}
+
+// A partial value: a plain store for the combine launch; for the fused
+// merge an agent-scope store, which writes through this XCD's L2 so that a
+// workgroup on another XCD can read it.
+__device__ __forceinline__ void store_partial(float* dst, float v, bool fused) {
+  if (fused) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *dst = v;
+}
+
+// Fused merge, run by every thread of a split workgroup after its partial
+// stores (the data-driven reduction of §4.3: no launch boundary between the
+// sweeps and the merge).  The partials were stored with agent-scope
+// (write-through) stores, and each thread waits until its own are
+// acknowledged -- that is what makes them visible on the other XCDs, whose
+// L2 caches are separate, without writing back a whole L2 as a release
+// fence would.  The workgroup then counts itself in, and the workgroup that
+// arrives last -- the one that sees n_split - 1 earlier arrivals --
+// invalidates its caches (an agent-scope acquire), merges the partials with
+// exactly the combine launch's code (so the results are bit-identical to
+// it), and resets the counter to zero for the next call.  `n_split` is this
+// sequence's split count: workgroups past its end return before writing a
+// partial and are not counted.
+template <typename OutT>
+__device__ __forceinline__ void fused_merge_tail(const DecodeParams& p, int b, int kvh,
+                                                 int n_split) {
+  __shared__ int s_last;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(p.counters + (size_t)b * p.H_kv + kvh, 1u,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)(n_split - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int M = p.G * p.T_q;
+  const int row0 = (b * p.H_q + kvh * p.G) * p.T_q;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int nwaves = blockDim.x >> 6;
+  // Wave w takes units w, w + nwaves, ... in batches whose first load
+  // rounds are all in flight together (at most ~96 registers of loads).
+  const int ng = combine_ng(p.n_split_max);
+  auto run = [&](auto ngc, auto uc) {
+    constexpr int NG = decltype(ngc)::value, U = decltype(uc)::value;
+    for (int base = wave; base < 4 * M; base += nwaves * U) {
+      int bhs[U], qs[U], count = 0;
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int u = min(base + nwaves * i, 4 * M - 1);
+        bhs[i] = row0 + (u >> 2);
+        qs[i] = u & 3;
+        count += base + nwaves * i < 4 * M;
+      }
+      combine_rows<OutT, NG, U>(p, bhs, qs, count, lane);
+    }
+  };
+  if (ng == 2) run(std::integral_constant<int, 2>(), std::integral_constant<int, 8>());
+  else if (ng == 4) run(std::integral_constant<int, 4>(), std::integral_constant<int, 4>());
+  else run(std::integral_constant<int, 8>(), std::integral_constant<int, 2>());
+  if (threadIdx.x == 0)
+    __hip_atomic_store(p.counters + (size_t)b * p.H_kv + kvh, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
 }  // namespace
 
 // Grid: (n_split_max, H_kv, B); block: 256 threads.  kPaged: K/V live in a
@@ -329,12 +557,14 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
       lacc += wt * sm_l[w][qn];
     }
     const size_t part = part0 + (size_t)qn * p.n_split_max;
-    p.ws_o[part * kD + dd] = acc;
+    const bool fused = p.counters != nullptr;
+    store_partial(p.ws_o + part * kD + dd, acc, fused);
     if (dd == 0) {
-      p.ws_ml[2 * part] = M;
-      p.ws_ml[2 * part + 1] = lacc;
+      store_partial(p.ws_ml + 2 * part, M, fused);
+      store_partial(p.ws_ml + 2 * part + 1, lacc, fused);
     }
   }
+  if (p.counters != nullptr) fused_merge_tail<__bf16>(p, b, kvh, (L + p.chunk - 1) / p.chunk);
 }
 
 // fp32 decode partial: one workgroup of 256 threads per 64-key split.  The
@@ -457,147 +687,22 @@ __global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p)
     const int n = n0 + 2 * u;
     if (n < p.G) {
       const size_t part = part0 + (size_t)n * p.n_split_max;
-      p.ws_o[part * kD + dd] = acc[u];
+      const bool fused = p.counters != nullptr;
+      store_partial(p.ws_o + part * kD + dd, acc[u], fused);
       if (dd == 0) {
-        p.ws_ml[2 * part] = sm[n];
-        p.ws_ml[2 * part + 1] = sl[n];
+        store_partial(p.ws_ml + 2 * part, sm[n], fused);
+        store_partial(p.ws_ml + 2 * part + 1, sl[n], fused);
       }
     }
   }
+  if (p.counters != nullptr) fused_merge_tail<float>(p, b, kvh, (L + kF32Chunk - 1) / kF32Chunk);
 }
 
-// Online log-sum-exp merge of split partials, NG at a time per lane so that
-// all of a group's loads are in flight together.  (M, acc, lacc) is the running
-// state; a group is folded in with the merge rule of §4: rescale both sides
-// to the larger max and add.
-struct MergeAcc {
-  float M;
-  f32x4 acc;
-  float lacc;
-};
 
-constexpr int kCombSlots = 8;     // split slots per wave (lane / 8)
-
-template <int NG>   // splits per lane and load round
-struct MergeLoads {
-  float m[NG], l[NG];
-  f32x4 o[NG];
-};
-
-// Loads splits s0, s0 + stride, ...; indices at or past `s_alloc` (the
-// partials the workspace holds per row) re-read the last one, so every load
-// is unconditional and all of them are in flight together.  Such splits lie
-// past the sequence's split count and are discarded by merge_fold.
-template <int NG>
-__device__ __forceinline__ void merge_load(MergeLoads<NG>& g, const float* ml, const float* po, int s0,
-                                           int s_alloc, int stride) {
-#pragma unroll
-  for (int u = 0; u < NG; ++u) {
-    const int s = min(s0 + u * stride, s_alloc - 1);
-    const f32x2 m2 = *reinterpret_cast<const f32x2*>(ml + 2 * s);
-    g.o[u] = *reinterpret_cast<const f32x4*>(po + (size_t)s * kD);
-    g.m[u] = m2[0];
-    g.l[u] = m2[1];
-  }
-}
-
-// Merges (m, acc, l) into `st` with the rule of §4.  Branch-free: with both
-// sides empty (m = -inf) the reference is 0 and both weights are 0.
-__device__ __forceinline__ void merge_pair(MergeAcc& st, float m, f32x4 acc, float l) {
-  const float gm = fmaxf(st.M, m);
-  const float ref = gm == kNegInf ? 0.f : gm;
-  const float c0 = fast_exp2(st.M - ref);
-  const float c1 = fast_exp2(m - ref);
-  st.acc = st.acc * c0 + acc * c1;
-  st.lacc = st.lacc * c0 + l * c1;
-  st.M = gm;
-}
-
-// Folds the loaded splits below `s_valid` (the splits of this call) into
-// `st`; the others are replaced by the identity (-inf, 0, 0) before use.
-template <int NG>
-__device__ __forceinline__ void merge_fold(MergeAcc& st, MergeLoads<NG>& g, int s0, int s_valid,
-                                           int stride) {
-#pragma unroll
-  for (int u = 0; u < NG; ++u) {
-    if (s0 + u * stride >= s_valid) {
-      g.m[u] = kNegInf;
-      g.l[u] = 0.f;
-      g.o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-  float gm = st.M;
-#pragma unroll
-  for (int u = 0; u < NG; ++u) gm = fmaxf(gm, g.m[u]);
-  // Branch-free (so that no load is sunk behind a branch): with every side
-  // empty, gm = -inf and the weights below are exp2(-inf) = 0.
-  const float ref = gm == kNegInf ? 0.f : gm;
-  const float c = fast_exp2(st.M - ref);
-  st.acc *= c;
-  st.lacc *= c;
-#pragma unroll
-  for (int u = 0; u < NG; ++u) {
-    const float w = fast_exp2(g.m[u] - ref);
-    st.acc += w * g.o[u];
-    st.lacc += w * g.l[u];
-  }
-  st.M = gm;
-}
-
-// Combine: one wave per (output row, quarter of d), rows being (sequence,
-// query head, token); the 4 waves of a row run on different CUs, so a row's
-// partials are fetched by four load pipelines at once.  Lane l takes split
-// slot j = l / 8 (splits j, j + 8, j + 16, ...) and output columns
-// 32*quarter + 4*(l % 8) .. +4; the 8 slots then merge across lanes
-// (xor 8, 16, 32).  Normalises once and rounds to the output dtype (the
-// final O / l of §4).  The first 8*NG splits' loads are issued together with
-// the sequence length's, so a call of up to 8*NG splits costs one memory
-// round trip; splits past the sequence's count are discarded after the
-// loads.  NG (2, 4 or 8) follows the workspace's split count, so that a row
-// with few splits does not load the same partial several times.
+// The combine launch: one wave per (folded row, quarter of d).
 template <typename OutT, int NG>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
-  const int bh = blockIdx.x;                 // folded row (sequence, head, token)
-  const int quarter = blockIdx.y;
-  const int b = bh / (p.H_q * p.T_q);
-  const int lane = threadIdx.x;
-  const int slot = lane >> 3;
-  const int d0 = 32 * quarter + 4 * (lane & 7);
-  const size_t part0 = (size_t)bh * p.n_split_max;
-  const float* ml = p.ws_ml + 2 * part0;
-  const float* po = p.ws_o + part0 * kD + d0;
-  const int len = p.kv_lens[b];
-  MergeLoads<NG> g;
-  merge_load(g, ml, po, slot, p.n_split_max, kCombSlots);
-  const int L = min(len, p.max_kv_len);
-  const int ns = (L + p.chunk - 1) / p.chunk;
-  MergeAcc st{kNegInf, {0.f, 0.f, 0.f, 0.f}, 0.f};
-  merge_fold(st, g, slot, ns, kCombSlots);
-  for (int s0 = slot + kCombSlots * NG; s0 < ns; s0 += kCombSlots * NG) {
-    merge_load(g, ml, po, s0, p.n_split_max, kCombSlots);
-    merge_fold(st, g, s0, ns, kCombSlots);
-  }
-#pragma unroll
-  for (int mask = 8; mask < 64; mask <<= 1) {
-    f32x4 ao;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ao[i] = __shfl_xor(st.acc[i], mask, 64);
-    const float mo = __shfl_xor(st.M, mask, 64);
-    const float lo = __shfl_xor(st.lacc, mask, 64);
-    merge_pair(st, mo, ao, lo);
-  }
-  if (slot == 0) {
-    const float inv = 1.f / st.lacc;
-    OutT* o = static_cast<OutT*>(p.o) + (size_t)bh * kD + d0;
-    if constexpr (sizeof(OutT) == 2) {
-      const u32x2 w = {pack_bf16x2(st.acc[0] * inv, st.acc[1] * inv),
-                       pack_bf16x2(st.acc[2] * inv, st.acc[3] * inv)};
-      *reinterpret_cast<u32x2*>(o) = w;
-    } else {
-      *reinterpret_cast<f32x4*>(o) = st.acc * inv;
-    }
-    if (p.lse != nullptr && lane == 0 && quarter == 0) p.lse[bh] = (st.M + __log2f(st.lacc)) * kLn2;
-  }
+  combine_row<OutT, NG>(p, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, int phases) {
@@ -619,9 +724,10 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, i
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (phases & kDecodeCombine) {
+  // With the fused merge the split kernel writes the outputs itself.
+  if ((phases & kDecodeCombine) && p.counters == nullptr) {
     const dim3 grid(p.B * p.H_q * p.T_q, 4);
-    const int ng = p.n_split_max <= 16 ? 2 : p.n_split_max <= 32 ? 4 : 8;
+    const int ng = combine_ng(p.n_split_max);
     if (bf16) {
       if (ng == 2) hipLaunchKernelGGL((decode_combine_kernel<__bf16, 2>), grid, dim3(64), 0, stream, p);
       else if (ng == 4) hipLaunchKernelGGL((decode_combine_kernel<__bf16, 4>), grid, dim3(64), 0, stream, p);

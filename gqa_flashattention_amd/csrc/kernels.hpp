@@ -30,6 +30,10 @@ struct DecodeParams {
   int max_pages;
   int page_shift;
   int num_pages;        // pool size; table entries are clamped into [0, num_pages)
+  // Fused merge (non-null): [B * H_kv] arrival counters, zero on entry and
+  // left zero.  The split kernel's last workgroup of each (sequence, KV
+  // head) merges that head's partials itself; no combine launch follows.
+  unsigned* counters;
 };
 
 struct PrefillParams {
@@ -79,6 +83,7 @@ hipError_t launch_merge(const MergeParams& p, bool bf16, hipStream_t stream);
 // Decode launches: the split partial kernel, the combine kernel, or both.
 constexpr int kDecodePartial = 1;
 constexpr int kDecodeCombine = 2;
+constexpr int kDecodeFused = 4;    // with kDecodePartial: the split kernel merges (counters set)
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, int phases);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 // Multi-token decode: its partial kernel (chosen by G * T_q) and/or the

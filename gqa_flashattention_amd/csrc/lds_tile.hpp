@@ -63,10 +63,5 @@ __device__ __forceinline__ void dma_load_x4(int voff, u32x4 rsrc, unsigned lds_d
                : "memory");
 }
 
-// s_waitcnt immediate that waits until at most `n` (0..63) vector memory
-// operations of this wave are outstanding (lgkm and exp counters ignored).
-constexpr unsigned vmcnt_imm(int n) {
-  return 0x0F70u | ((unsigned)n & 15u) | (((unsigned)n >> 4) << 14);
-}
 
 }  // namespace gqa

@@ -114,8 +114,9 @@ int gqa_attn_decode_split_tokens(int B, int H_kv, int max_kv_len,
                                  int chunk_tokens, int dtype);
 
 /*
- * Device workspace (bytes) gqa_attn_decode needs: one unnormalised partial
- * (m, l, O[d]) in float32 per (sequence, query head, split), the
+ * Device workspace (bytes) gqa_attn_decode needs: a fixed 64 KiB of arrival
+ * counters (used only by gqa_attn_decode_fused), then one unnormalised
+ * partial (m, l, O[d]) in float32 per (sequence, query head, split), the
  * (m_i, l_i, O_i) of §4.  Returns 0 on invalid arguments.
  */
 size_t gqa_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int d,
@@ -155,6 +156,41 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                     int B, int H_q, int H_kv, int d, int kv_cap,
                     int max_kv_len, float scale, int dtype, int chunk_tokens,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_attn_decode in ONE launch: the data-driven reduction of §4.3 ("no
+ * global barrier").  Each split workgroup publishes its partial and counts
+ * itself in on its (sequence, KV head)'s arrival counter; the workgroup
+ * that arrives last merges that head's partials with the same code and in
+ * the same order as the combine launch, so the results are bit-identical
+ * to gqa_attn_decode's for the same chunk_tokens.  Same arguments and
+ * workspace size as gqa_attn_decode, with one extra contract:
+ *
+ *  - The arrival counters are the workspace's first 64 KiB (one uint32 per
+ *    (sequence, KV head); B * H_kv <= 16384, else GQA_ERR_UNSUPPORTED).
+ *    They must be zero before the workspace's FIRST fused call -- zero-fill
+ *    it once when it is allocated -- and every fused call leaves them zero
+ *    again; no decode entry point writes them otherwise, whatever the
+ *    shape, so one workspace serves fused and two-launch calls of any
+ *    shape.  After a call that did not complete (a fault), zero it again.
+ *  - Calls sharing a workspace must not overlap in time (as for
+ *    gqa_attn_decode).
+ *
+ * Cost on MI355X: the partials are published with write-through
+ * (agent-scope) stores, each workgroup waits for their acknowledgement and
+ * counts in with one atomic, and the last arriver invalidates its caches
+ * before merging -- the other splits may have run on any of the 8 XCDs,
+ * whose L2 caches are separate.  Measured, that tail costs more than the
+ * second launch of gqa_attn_decode at every size tried (a 256-key fp32
+ * call, a 32K-key call, the 8K-128K ragged batch), so gqa_attn_decode stays
+ * the faster default; this entry point is for callers that want exactly
+ * one kernel per decode step.
+ */
+int gqa_attn_decode_fused(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* kv_lens, void* o, float* lse,
+                          int B, int H_q, int H_kv, int d, int kv_cap,
+                          int max_kv_len, float scale, int dtype, int chunk_tokens,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gqa_attn_decode for callers that cannot allocate device memory (code under
