@@ -214,6 +214,50 @@ def time_decode_workload(name, steps, warmup):
     b2b_us = e[0].elapsed_time(e[1]) * 1e3 / steps
     part_us = e[2].elapsed_time(e[3]) * 1e3 / steps
     fused_us = e[4].elapsed_time(e[5]) * 1e3 / steps
+    graph = None
+    if w.kv_bytes() < (16 << 20):
+        # A short call is bound by the host's issue rate (about 10 us per
+        # call through the binding), not by the GPU: replay `steps` calls
+        # captured in one HIP graph to time the GPU side, after checking
+        # that a replay reproduces the eager result bit for bit.
+        x0 = copies[0]
+        ref = out.clone()
+        gq.decode(x0["q"], x0["k"], x0["v"], x0["kv_lens"], max_kv_len=w.max_kv_len,
+                  scale=w.scale, out=ref, workspace=ws)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    x = copies[i % ncopies]
+                    gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=w.max_kv_len,
+                              scale=w.scale, out=out, workspace=ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gms = []
+        for r in range(4):
+            out.zero_()
+            ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ga.record()
+            g.replay()
+            gb.record()
+            torch.cuda.synchronize()
+            gms.append(ga.elapsed_time(gb))
+            # The last captured call used copies[(steps - 1) % ncopies].
+            last = copies[(steps - 1) % ncopies]
+            want = torch.empty_like(out)
+            gq.decode(last["q"], last["k"], last["v"], last["kv_lens"], max_kv_len=w.max_kv_len,
+                      scale=w.scale, out=want, workspace=torch.empty_like(ws))
+            torch.cuda.synchronize()
+            if not torch.equal(out, want):
+                raise RuntimeError(f"{name}: graph replay {r} differs from the eager call")
+        graph = {"us_per_call": round(sorted(gms)[len(gms) // 2] * 1e3 / steps, 3),
+                 "calls_per_graph": steps, "replays": len(gms),
+                 "kind": "gqa_attn_decode calls captured in one HIP graph and replayed "
+                         "(median replay / calls); each replay checked bitwise against an "
+                         "eager call"}
+        del g
     gbs = w.decode_bytes() / (b2b_us * 1e-6) / 1e9
     part_bytes = w.kv_bytes() + w.B * w.H_q * w.T_q * w.d * w.elem_bytes
     part_gbs = part_bytes / (part_us * 1e-6) / 1e9
@@ -227,6 +271,7 @@ def time_decode_workload(name, steps, warmup):
            "fused": {"entry_point": "gqa_attn_decode_fused",
                      "us_per_call_back_to_back": round(fused_us, 3),
                      "GB_s": round(w.decode_bytes() / (fused_us * 1e-6) / 1e9, 2)},
+           "graph_replay": graph,
            "roofline": {"bound": "hbm" if w.dtype == "bf16" else "latency",
                         "kernel": f"decode_partial_{w.dtype}_kernel",
                         "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -597,6 +597,7 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float
   p.heads_per_wg = hpw;
   p.n_qblk = (int)n_qblk;
   p.q_negate = scale < 0.f;
+  p.pair_blocks = causal ? 1 : 0;
   p.scale_log2 = fabsf(scale) * 1.4426950408889634f;
   p.cu_seqlens_q = nullptr;
   p.kv_lens = nullptr;
@@ -663,6 +664,7 @@ static int prefill_varlen_common(const void* q, const void* k, const void* v,
   p.heads_per_wg = hpw;
   p.n_qblk = (int)n_qblk;
   p.q_negate = scale < 0.f;
+  p.pair_blocks = 0;
   p.scale_log2 = fabsf(scale) * 1.4426950408889634f;
   p.cu_seqlens_q = cu_seqlens_q;
   p.kv_lens = kv_lens;

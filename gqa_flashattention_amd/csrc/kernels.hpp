@@ -47,6 +47,7 @@ struct PrefillParams {
   int heads_per_wg;     // query heads of one KV group per workgroup: gcd(G, waves)
   int n_qblk;           // position blocks: ceil(S_q / (32 * waves / heads_per_wg))
   int q_negate;         // 1 when the softmax scale is negative (Q's sign is flipped)
+  int pair_blocks;      // dense causal: each workgroup runs a query block and its mirror
   float scale_log2;     // |scale| * log2(e)
   // Varlen batch (both null otherwise): q/o are [S_q = total_q, H_q, d],
   // lse [total_q, H_q]; sequence b's chunk is rows cu_seqlens_q[b] ..

@@ -43,7 +43,9 @@
 // Workgroup order: the KV head is the fastest-varying index, so with the
 // round-robin dispatch of workgroups over the 8 XCDs each KV head's tiles
 // stay in one XCD's L2; query blocks go heaviest (longest causal prefix)
-// first.
+// first.  A causal dense launch pairs each block with its mirror in one
+// workgroup (the heaviest with the lightest, and so on): every workgroup
+// then does about the same work, and half as many workgroups start.
 //
 // Varlen batches (chunks of several sequences in one launch, each the newest
 // positions of its sequence): the same kernel, with each workgroup reading
@@ -168,7 +170,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int gamma = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 
-  const Place pl = locate(p, blockIdx.x, wv);
+  // One 32-position block (of each wave's head) from start to end; `vid` is
+  // the block's workgroup id in the unpaired grid.  The body is not
+  // re-indented inside the lambda.
+  auto run_block = [&](const int vid) __attribute__((always_inline)) {
+  const Place pl = locate(p, vid, wv);
   const int b = pl.b, kvh = pl.kvh, P0 = pl.P0, qw0 = pl.qw0;
   const int S_q = pl.S_q, S_kv = pl.S_kv, offset = pl.offset, qstride = pl.qstride;
   const size_t qrow0 = pl.qrow0;
@@ -182,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     // nothing.  The rows are addressed from opaque copies of the ids, as in
     // the epilogue: this block is laid out after the main loop, and values
     // shared with the loop's prologue would otherwise stay live across it.
-    int tid_z = threadIdx.x, bid_z = blockIdx.x;
+    int tid_z = threadIdx.x, bid_z = vid;
     asm volatile("" : "+v"(tid_z), "+s"(bid_z));
     const Place pz = locate(p, bid_z, __builtin_amdgcn_readfirstlane(tid_z >> 6));
     const int qrow_z = pz.qw0 + (tid_z & 31), h2_z = (tid_z >> 5) & 1;
@@ -622,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // arguments from the kernarg segment, where this kernel's only argument
   // sits at offset 0), so the row addressing is recomputed here rather than
   // held in registers through the loop.
-  int tid_e = threadIdx.x, bid_e = blockIdx.x;
+  int tid_e = threadIdx.x, bid_e = vid;
   typedef const __attribute__((address_space(4))) PrefillParams KernargParams;
   KernargParams* pk = (KernargParams*)__builtin_amdgcn_kernarg_segment_ptr();
   asm volatile("" : "+v"(tid_e), "+s"(bid_e), "+s"(pk));
@@ -657,6 +663,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int qrow_e = pe.qw0 + c_e;
   if (qrow_e < pe.S_q && pa.lse != nullptr && h2_e == 0)
     pa.lse[pe.qrow0 + (size_t)qrow_e * pe.qstride] = (m_ref + __log2f(lsum)) * kLn2;
+  };
+
+  // Causal dense launches pair each query block with its mirror (the
+  // heaviest with the lightest, ...), so every workgroup does about the
+  // same work and the grid has half as many workgroups.  A block's id is
+  // its workgroup id in the unpaired grid; the second one is derived from an
+  // opaque copy of the workgroup id, so nothing of the first block's
+  // addressing stays live through it.
+  if (kVarlen || !p.pair_blocks) {
+    run_block((int)blockIdx.x);
+    return;
+  }
+  {
+    const int per_rank = p.H_kv * (p.G / p.heads_per_wg) * p.B;
+    run_block((int)(blockIdx.x % per_rank + per_rank * (blockIdx.x / per_rank)));
+  }
+  int bid2 = blockIdx.x;
+  asm volatile("" : "+s"(bid2));
+  typedef const __attribute__((address_space(4))) PrefillParams KernargParams2;
+  KernargParams2* pk2 = (KernargParams2*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(pk2));
+  const int per_rank2 = pk2->H_kv * (pk2->G / pk2->heads_per_wg) * pk2->B;
+  const int rank2 = pk2->n_qblk - 1 - bid2 / per_rank2;
+  if (rank2 == bid2 / per_rank2) return;   // the middle block of an odd count
+  __syncthreads();   // the first block's output staging in sK has been read
+  run_block(bid2 % per_rank2 + per_rank2 * rank2);
 }
 
 // Tile count of a varlen work item (b, pblk): the key tiles its workgroup
@@ -786,7 +818,8 @@ int prefill_heads_per_wg(int G) {
 int prefill_rows_per_wg() { return 32 * kWaves; }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  const long long nwg = (long long)p.n_qblk * p.B * p.H_kv * (p.G / p.heads_per_wg);
+  const long long nblk = p.pair_blocks && p.cu_seqlens_q == nullptr ? (p.n_qblk + 1) / 2 : p.n_qblk;
+  const long long nwg = nblk * p.B * p.H_kv * (p.G / p.heads_per_wg);
   if (p.cu_seqlens_q != nullptr) {
     int shift = 0;
     while ((((long long)p.S_kv + kBN - 1) / kBN >> shift) >= kSchedBins) ++shift;
