@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of each oracle sample")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="do not time gqa_attn_decode_fused (its launches share the split "
+                         "kernel's name, so profiler runs of the two-launch path leave it out)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other measured workloads and the copy ceiling after the "
                          "headline steps")
@@ -577,7 +580,7 @@ def main():
     kd = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     kp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     kf = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    fused_ok = do_dec and not multi and not paged
+    fused_ok = do_dec and not multi and not paged and not args.no_fused
     if fused_ok:
         for i in range(min(args.warmup, 20)):
             decode_call(i, "fused")
