@@ -68,8 +68,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of each oracle sample")
     ap.add_argument("--no-fused", action="store_true",
-                    help="do not time gqa_attn_decode_fused (its launches share the split "
-                         "kernel's name, so profiler runs of the two-launch path leave it out)")
+                    help="do not time gqa_attn_decode_fused (a shorter run; its launches "
+                         "are decode_fused_bf16_kernel, apart from the two-launch kernels)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other measured workloads and the copy ceiling after the "
                          "headline steps")

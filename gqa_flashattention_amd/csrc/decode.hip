@@ -11,7 +11,9 @@
 // GPU mapping.  One workgroup = 4 waves = one contiguous split of
 // `chunk` keys of one (sequence, KV head); wave w sweeps the w-th quarter of
 // the split in blocks of 32 keys, straight from HBM into registers (K and V
-// are read exactly once, so they bypass LDS).  Scores are computed
+// are read exactly once, so they bypass LDS).  Each wave reads one address
+// stream: the K rows of two blocks, then their V rows, and so on, with the
+// online-softmax update once per two blocks.  Scores are computed
 // transposed, S^T = K . Q^T, on the 16x16x32 bf16 MFMA with keys in M and
 // the (zero-padded) G <= 16 query heads in N; O^T = V^T . P^T uses the same
 // MFMA with d in M.  The 8x8 transpose V needs is done in registers by byte
@@ -40,58 +42,21 @@ constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kBlk = 32;  // keys per wave step
 
-// Loads of one 32-key block for one lane.
-//   k[sb][kb]: K row (key0 + 16*sb + l%16), d range 32*kb + 8*(l/16) .. +8
-//              -> A operand of S^T tile sb, k-step kb.
-//   v[j]:      V row key(g, j), d range 8*(l%16) .. +8, where
-//                 key(g, j) = 4g + j (j < 4) or 16 + 4g + (j - 4) (j >= 4):
-//                 the keys this lane's P^T slots hold.
-struct Block {
-  u32x4 k[2][4];
-  u32x4 v[8];
-};
+// One lane's loads of one 32-key block of K or of V: eight 16-byte pieces
+// (a register slot holds either).
+//   K: piece 4*sb + kb = K row (key0 + 16*sb + l%16), d range
+//      32*kb + 8*(l/16) .. +8 -> A operand of S^T tile sb, k-step kb.
+//   V: piece j = V row key(g, j), d range 8*(l%16) .. +8, where
+//      key(g, j) = 4g + j (j < 4) or 16 + 4g + (j - 4) (j >= 4): the keys
+//      this lane's P^T slots hold.
+typedef u32x4 Slot[8];
 
 // Per-lane byte offsets of a block's loads relative to the block's first
-// key; the block's own offset goes in the scalar offset of the load.
+// key (the block's own offset is added to them).
 struct BlockOffsets {
   int k[2];   // K row l%16 (+16 rows for sb = 1), d = 8*(l/16)
   int v[2];   // V row 4*(l/16) (+16 rows for j >= 4), d = 8*(l%16)
 };
-
-// The wave's K and V rows go through buffer resources that end at the
-// wave's last key: rows past it read as zeros without touching memory, so
-// a partial last block needs no guarded loads (its keys are masked, and its
-// zero V rows meet zero weights).  Nontemporal: each byte is read once.
-__device__ __forceinline__ void load_block(Block& blk, __amdgpu_buffer_rsrc_t rk,
-                                           __amdgpu_buffer_rsrc_t rv, const BlockOffsets& off,
-                                           int soff) {
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      blk.k[sb][kb] = __builtin_amdgcn_raw_buffer_load_b128(rk, off.k[sb] + 64 * kb, soff, 2);
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    blk.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, off.v[j >> 2] + (j & 3) * kD * 2, soff, 2);
-}
-
-// Paged cache: the two 16-key sub-blocks of a block each lie in one page
-// (page sizes are powers of two >= 16 and blocks start at multiples of 32),
-// so each gets its own resources: base = the sub-block's first row in its
-// page, size = the sub-block's rows below the wave's last key (0 when the
-// sub-block starts past it: all loads then read zeros).
-__device__ __forceinline__ void load_block_paged(Block& blk, const __amdgpu_buffer_rsrc_t (&rk)[2],
-                                                 const __amdgpu_buffer_rsrc_t (&rv)[2],
-                                                 const BlockOffsets& off) {
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      blk.k[sb][kb] = __builtin_amdgcn_raw_buffer_load_b128(rk[sb], off.k[0] + 64 * kb, 0, 2);
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    blk.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv[j >> 2], off.v[0] + (j & 3) * kD * 2, 0, 2);
-}
 
 // Running state of one wave: query n = lane % 16 (rows >= G are padding).
 struct State {
@@ -100,72 +65,28 @@ struct State {
   f32x4 o[8];    // O^T, d-tile dt: lane holds d = 8*(4*(lane/16)+i) + dt, query n
 };
 
-// `masked` (wave-uniform) is set for a block that holds keys some row may
-// not see: keys at or past `kend` (a partial last block), or past the
-// lane's row limit `vis_last` (the causal tail of a multi-token decode).
-// Such keys get weight 0.
-__device__ __forceinline__ void fold_block(State& st, const Block& blk, const bf16x8 (&qb)[4],
-                                           int key0, int kend, int vis_last, float scale_log2,
-                                           int lane, bool masked) {
-  const int g = lane >> 4;
-  // S^T = K . Q^T for two 16-key sub-blocks.
-  f32x4 s[2];
+// S^T = K . Q^T for the block's two 16-key sub-blocks.
+__device__ __forceinline__ void block_scores(f32x4 (&s)[2], const Slot& k, const bf16x8 (&qb)[4]) {
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(blk.k[sb][kb]), qb[kb], s[sb], 0, 0, 0);
+      s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[4 * sb + kb]), qb[kb], s[sb], 0, 0, 0);
   }
-  // Scale into the log2 domain; mask keys past the end (partial block only).
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) s[sb] *= scale_log2;
-  if (masked) {
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (key0 + 16 * sb + 4 * g + i >= kend || key0 + 16 * sb + 4 * g + i > vis_last)
-          s[sb][i] = kNegInf;
-  }
-  float bmax = kNegInf;
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[sb][i]);
-  bmax = wave_max_xor(bmax, 16);
-  bmax = wave_max_xor(bmax, 32);
-  const float m_new = fmaxf(st.m, bmax);
-  // A row that has seen no visible key yet keeps m = -inf; its weights are
-  // taken against 0 (all exp2(-inf) = 0) so that no -inf - -inf appears.
-  const float mref = m_new == kNegInf ? 0.f : m_new;
-  const float corr = fast_exp2(st.m - mref);  // 0 on a row's first visible block (m = -inf)
-  float psum = 0.f;
-  float p[2][4];
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[sb][i] = fast_exp2(s[sb][i] - mref);
-      psum += p[sb][i];
-    }
-  st.l = st.l * corr + psum;
-  st.m = m_new;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) st.o[dt] *= corr;
-  // P^T operand: slots 0..3 = sub-block 0 keys 4g+i, slots 4..7 = sub-block 1.
-  u32x4 pw = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-              pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
-  const bf16x8 pb = as_bf16x8(pw);
-  // V^T operand for d-tile dt: element j = V[key(g, j)][8*(lane%16) + dt].
+}
+
+// O^T += V^T . P^T.  V^T operand for d-tile dt: element j =
+// V[key(g, j)][8*(lane%16) + dt].
+__device__ __forceinline__ void block_pv(State& st, const Slot& v, bf16x8 pb) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     const int w = dt >> 1;
     u32x4 a;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const unsigned int lo = blk.v[2 * jj][w];
-      const unsigned int hi = blk.v[2 * jj + 1][w];
+      const unsigned int lo = v[2 * jj][w];
+      const unsigned int hi = v[2 * jj + 1][w];
       // One byte permute: the low (dt even) or high (dt odd) halves of
       // lo and hi, lo's in the low half of the result.
       a[jj] = __builtin_amdgcn_perm(hi, lo, (dt & 1) ? 0x07060302u : 0x05040100u);
@@ -400,12 +321,12 @@ __device__ __forceinline__ void fused_merge_tail(const DecodeParams& p, int b, i
     __hip_atomic_store(p.counters + (size_t)b * p.H_kv + kvh, 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
-}  // namespace
-
-// Grid: (n_split_max, H_kv, B); block: 256 threads.  kPaged: K/V live in a
-// page pool addressed through the block table (DecodeParams::block_table).
-template <bool kPaged>
-__global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParams p) {
+// The bf16 split sweep.  Grid: (n_split_max, H_kv, B); block: 256
+// threads.  kPaged: K/V live in a page pool addressed through the block
+// table (DecodeParams::block_table).  kFused: the one-launch decode
+// (DecodeParams::counters set) merges the partials at the end.
+template <bool kPaged, bool kFused>
+__device__ __forceinline__ void decode_partial_bf16(const DecodeParams& p) {
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
@@ -451,7 +372,6 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
     // loads are in flight while the current block is folded.  Only the
     // last block of the wave's range can be partial (masked).
     const int nblk = (we - ws + kBlk - 1) / kBlk;
-    const bool tail = (we - ws) % kBlk != 0;
     const unsigned bytes = kPaged ? 0u : (unsigned)(we - ws) * (kD * 2);
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (size_t)ws * kD), (short)0, bytes, 0x00020000);
@@ -474,45 +394,159 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
       const int npg = ((we - 1) >> shift) - lp0 + 1;
       if (lane < npg) pt = min(max(p.block_table[(size_t)b * p.max_pages + lp0 + lane], 0), p.num_pages - 1);
     }
-    Block A, B;
-    auto load_i = [&](Block& bl, int i) {
-      if constexpr (kPaged) {
-        const size_t page_elems = (size_t)p.H_kv * (kD << shift);
-        const size_t head_elems = (size_t)kvh * (kD << shift);
-        __amdgpu_buffer_rsrc_t rks[2], rvs[2];
+    // Paged: the resources of block i's two 16-key sub-blocks.
+    auto paged_rsrc = [&](const __bf16* base, int i, __amdgpu_buffer_rsrc_t (&r)[2])
+                          __attribute__((always_inline)) {
+      const size_t page_elems = (size_t)p.H_kv * (kD << shift);
+      const size_t head_elems = (size_t)kvh * (kD << shift);
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          const int pos = ws + i * kBlk + 16 * sb;
-          // readfirstlane: the page is wave-uniform, and saying so keeps the
-          // resources in scalar registers (no per-lane loop around the loads).
-          const int pp = __builtin_amdgcn_readfirstlane(
-              __builtin_amdgcn_readlane(pt, min((pos >> shift) - lp0, 63)));
-          const size_t e = (size_t)pp * page_elems + head_elems + (size_t)(pos & ((1 << shift) - 1)) * kD;
-          const unsigned nb = __builtin_amdgcn_readfirstlane((unsigned)max(0, min(16, we - pos)) * (kD * 2));
-          rks[sb] = __builtin_amdgcn_make_buffer_rsrc(
-              (void*)(static_cast<const __bf16*>(p.k) + e), (short)0, nb, 0x00020000);
-          rvs[sb] = __builtin_amdgcn_make_buffer_rsrc(
-              (void*)(static_cast<const __bf16*>(p.v) + e), (short)0, nb, 0x00020000);
-        }
-        load_block_paged(bl, rks, rvs, off);
-      } else {
-        load_block(bl, rk, rv, off, i * kBlk * kD * 2);
+      for (int sb = 0; sb < 2; ++sb) {
+        const int pos = ws + i * kBlk + 16 * sb;
+        // readfirstlane: the page is wave-uniform, and saying so keeps the
+        // resources in scalar registers (no per-lane loop around the loads).
+        const int pp = __builtin_amdgcn_readfirstlane(
+            __builtin_amdgcn_readlane(pt, min((pos >> shift) - lp0, 63)));
+        const size_t e = (size_t)pp * page_elems + head_elems + (size_t)(pos & ((1 << shift) - 1)) * kD;
+        const unsigned nb = __builtin_amdgcn_readfirstlane((unsigned)max(0, min(16, we - pos)) * (kD * 2));
+        r[sb] = __builtin_amdgcn_make_buffer_rsrc((void*)(base + e), (short)0, nb, 0x00020000);
       }
     };
-    // Blocks that reach past L - T_q hold keys hidden from some rows.
-    const int first_hidden = L - p.T_q + 1;
-    auto fold_i = [&](const Block& bl, int i) {
-      const int key0 = ws + i * kBlk;
-      fold_block(st, bl, qb, key0, we, vis_last, p.scale_log2, lane,
-                 (tail && i == nblk - 1) || key0 + kBlk > first_hidden);
+    // One stream per wave.  The wave reads the K rows of a super-block of
+    // kSblk blocks, then their V rows, then the next super-block's K rows,
+    // with two blocks' loads (16 KiB) in flight in two register slots.
+    // Measured on MI355X: a wave that streams K and V side by side (two
+    // concurrent address streams) gets its bytes later than one that reads
+    // them one after the other, and a super-block of two blocks is the
+    // largest whose scores fit the registers of three waves per SIMD.
+    constexpr int kSblk = 2;
+    Slot slot[2];
+    // Issues the loads of stream item `it` of super-block q into `dst`; `it`
+    // is a compile-time position: 0..kSblk-1 are the K blocks, kSblk ..
+    // 2*kSblk-1 the V blocks, and later positions the next super-block's K
+    // blocks.  Blocks past the wave's range read zeros (the resources end at
+    // its last key), so the loads are unconditional and every wait the
+    // compiler inserts is for the one block consumed next.
+    auto issue = [&](Slot& dst, int q, int it) __attribute__((always_inline)) {
+      const bool isv = it >= kSblk && it < 2 * kSblk;
+      const int blk = it < kSblk ? q * kSblk + it
+                      : isv      ? q * kSblk + it - kSblk
+                                 : (q + 1) * kSblk + it - 2 * kSblk;
+      if constexpr (kPaged) {
+        __amdgpu_buffer_rsrc_t r[2];
+        paged_rsrc(static_cast<const __bf16*>(isv ? p.v : p.k), blk, r);
+        if (!isv) {
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+              dst[4 * sb + kb] = __builtin_amdgcn_raw_buffer_load_b128(r[sb], off.k[0] + 64 * kb, 0, 2);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            dst[j] = __builtin_amdgcn_raw_buffer_load_b128(r[j >> 2], off.v[0] + (j & 3) * kD * 2, 0, 2);
+        }
+      } else {
+        const int boff = blk * (kBlk * kD * 2);
+        if (!isv) {
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+            const int vo = off.k[sb] + boff;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+              dst[4 * sb + kb] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * kb, 0, 2);
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int vo = off.v[h] + boff;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              dst[4 * h + j] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + j * kD * 2, 0, 2);
+          }
+        }
+      }
     };
-    load_i(A, 0);
-    for (int i = 0; i < nblk; i += 2) {
-      if (i + 1 < nblk) load_i(B, i + 1);
-      fold_i(A, i);
-      if (i + 1 >= nblk) break;
-      if (i + 2 < nblk) load_i(A, i + 2);
-      fold_i(B, i + 1);
+    // Super-blocks that reach past L - T_q hold keys hidden from some rows.
+    const int first_hidden = L - p.T_q + 1;
+    const int nsb = (nblk + kSblk - 1) / kSblk;
+    issue(slot[0], 0, 0);
+    issue(slot[1], 0, 1);
+    for (int q = 0; q < nsb; ++q) {
+      const int key0 = ws + q * kSblk * kBlk;
+      // Scores of the super-block; each slot is refilled once read.
+      f32x4 s[kSblk][2];
+#pragma unroll
+      for (int it = 0; it < kSblk; ++it) {
+        Slot k;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) k[j] = slot[it & 1][j];
+        block_scores(s[it], k, qb);
+        issue(slot[it & 1], q, it + 2);
+      }
+      // The online-softmax update of §3 over the super-block: one new max,
+      // one rescale of l and O.  Keys at or past the wave's end, or past a
+      // row's limit `vis_last` (the causal tail of a multi-token decode),
+      // get weight 0; only a super-block that holds such keys is masked.
+      const int key_end = key0 + kSblk * kBlk;
+      const bool masked = key_end > we || key_end > first_hidden;
+#pragma unroll
+      for (int it = 0; it < kSblk; ++it)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) s[it][sb] *= p.scale_log2;
+      if (masked) {
+#pragma unroll
+        for (int it = 0; it < kSblk; ++it)
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = key0 + it * kBlk + 16 * sb + 4 * g + i;
+              if (key >= we || key > vis_last) s[it][sb][i] = kNegInf;
+            }
+      }
+      float bmax = kNegInf;
+#pragma unroll
+      for (int it = 0; it < kSblk; ++it)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[it][sb][i]);
+      bmax = wave_max_xor(bmax, 16);
+      bmax = wave_max_xor(bmax, 32);
+      const float m_new = fmaxf(st.m, bmax);
+      // A row that has seen no visible key yet keeps m = -inf; its weights
+      // are taken against 0 (all exp2(-inf) = 0) so that no -inf - -inf appears.
+      const float mref = m_new == kNegInf ? 0.f : m_new;
+      const float corr = fast_exp2(st.m - mref);  // 0 on a row's first visible keys (m = -inf)
+      float psum = 0.f;
+      bf16x8 pb[kSblk];   // P^T operands: slots 0..3 = sub-block 0 keys 4g+i, 4..7 = sub-block 1
+#pragma unroll
+      for (int it = 0; it < kSblk; ++it) {
+        float pr[2][4];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pr[sb][i] = fast_exp2(s[it][sb][i] - mref);
+            psum += pr[sb][i];
+          }
+        const u32x4 pw = {pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
+                          pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
+        pb[it] = as_bf16x8(pw);
+      }
+      st.l = st.l * corr + psum;
+      st.m = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) st.o[dt] *= corr;
+      // P.V of the super-block; each slot is refilled once read.
+#pragma unroll
+      for (int it = kSblk; it < 2 * kSblk; ++it) {
+        Slot v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = slot[it & 1][j];
+        block_pv(st, v, pb[it - kSblk]);
+        issue(slot[it & 1], q, it + 2);
+      }
     }
   }
 
@@ -557,14 +591,27 @@ __global__ __launch_bounds__(256, 2) void decode_partial_bf16_kernel(DecodeParam
       lacc += wt * sm_l[w][qn];
     }
     const size_t part = part0 + (size_t)qn * p.n_split_max;
-    const bool fused = p.counters != nullptr;
-    store_partial(p.ws_o + part * kD + dd, acc, fused);
+    store_partial(p.ws_o + part * kD + dd, acc, kFused);
     if (dd == 0) {
-      store_partial(p.ws_ml + 2 * part, M, fused);
-      store_partial(p.ws_ml + 2 * part + 1, lacc, fused);
+      store_partial(p.ws_ml + 2 * part, M, kFused);
+      store_partial(p.ws_ml + 2 * part + 1, lacc, kFused);
     }
   }
-  if (p.counters != nullptr) fused_merge_tail<__bf16>(p, b, kvh, (L + p.chunk - 1) / p.chunk);
+  if constexpr (kFused) fused_merge_tail<__bf16>(p, b, kvh, (L + p.chunk - 1) / p.chunk);
+}
+}  // namespace
+
+// The two-launch split kernel fits three waves per SIMD (at most 168
+// registers); the one-launch kernel, whose merge tail needs more registers,
+// is a kernel of its own at two waves per SIMD.
+template <bool kPaged>
+__global__ __launch_bounds__(256, 3) void decode_partial_bf16_kernel(DecodeParams p) {
+  decode_partial_bf16<kPaged, false>(p);
+}
+
+template <bool kPaged>
+__global__ __launch_bounds__(256, 2) void decode_fused_bf16_kernel(DecodeParams p) {
+  decode_partial_bf16<kPaged, true>(p);
 }
 
 // fp32 decode partial: one workgroup of 256 threads per 64-key split.  The
@@ -709,8 +756,13 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, i
   if (phases & kDecodePartial) {
     dim3 grid(p.n_split_max, p.H_kv, p.B);
     if (bf16) {
-      if (p.block_table != nullptr)
+      const bool paged = p.block_table != nullptr, fused = p.counters != nullptr;
+      if (paged && fused)
+        hipLaunchKernelGGL(decode_fused_bf16_kernel<true>, grid, dim3(256), 0, stream, p);
+      else if (paged)
         hipLaunchKernelGGL(decode_partial_bf16_kernel<true>, grid, dim3(256), 0, stream, p);
+      else if (fused)
+        hipLaunchKernelGGL(decode_fused_bf16_kernel<false>, grid, dim3(256), 0, stream, p);
       else
         hipLaunchKernelGGL(decode_partial_bf16_kernel<false>, grid, dim3(256), 0, stream, p);
     } else {
