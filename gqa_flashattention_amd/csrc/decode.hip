@@ -368,9 +368,8 @@ __device__ __forceinline__ void decode_partial_bf16(const DecodeParams& p) {
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (ws < we) {
-    // Two register buffers, A and B, alternate so that the next block's
-    // loads are in flight while the current block is folded.  Only the
-    // last block of the wave's range can be partial (masked).
+    // Blocks of 32 keys; only the last one of the wave's range can be
+    // partial (its keys past the range are masked).
     const int nblk = (we - ws + kBlk - 1) / kBlk;
     const unsigned bytes = kPaged ? 0u : (unsigned)(we - ws) * (kD * 2);
     const __amdgpu_buffer_rsrc_t rk =
