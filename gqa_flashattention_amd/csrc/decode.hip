@@ -330,13 +330,26 @@ __device__ __forceinline__ void decode_partial_bf16(const DecodeParams& p) {
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const int L = min(p.kv_lens[b], p.max_kv_len);
-  const int start = split * p.chunk;
-  if (start >= L) return;
-  const int end = min(start + p.chunk, L);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int lane = threadIdx.x & 63;
   const int quarter = p.chunk / kWaves;
+  const int start = split * p.chunk;
+  // Paged: lane j fetches the block-table entry of the wave's logical page
+  // lp0 + j (at most 64 pages per wave range, checked on the host).  The
+  // wave's first page follows from the split alone, so this load is issued
+  // together with the sequence length's rather than after it; entries past
+  // the table row are clamped to its last one, and those past the sequence
+  // are not used.
+  const int lp0 = (start + wave * quarter) >> p.page_shift;
+  int pt_raw = 0;
+  if constexpr (kPaged)
+    pt_raw = p.block_table[(size_t)b * p.max_pages + min(lp0 + lane, p.max_pages - 1)];
+  const int L = min(p.kv_lens[b], p.max_kv_len);
+  // Keeps the table load above the early exit below (the compiler would
+  // otherwise sink it there, behind the length's round trip).
+  if constexpr (kPaged) asm volatile("" : "+v"(pt_raw));
+  if (start >= L) return;
+  const int end = min(start + p.chunk, L);
   const int ws = start + wave * quarter;
   const int we = min(ws + quarter, end);
 
@@ -385,13 +398,12 @@ __device__ __forceinline__ void decode_partial_bf16(const DecodeParams& p) {
       off.v[1] = off.v[0] + 16 * (kD * 2);
     }
     // Paged: lane j holds the physical page of the wave's logical page
-    // lp0 + j (at most 64 pages per wave range, checked on the host).
+    // lp0 + j, clamped into the pool.
     const int shift = p.page_shift;
-    const int lp0 = ws >> shift;
     int pt = 0;
     if constexpr (kPaged) {
       const int npg = ((we - 1) >> shift) - lp0 + 1;
-      if (lane < npg) pt = min(max(p.block_table[(size_t)b * p.max_pages + lp0 + lane], 0), p.num_pages - 1);
+      if (lane < npg) pt = min(max(pt_raw, 0), p.num_pages - 1);
     }
     // Paged: the resources of block i's two 16-key sub-blocks.
     auto paged_rsrc = [&](const __bf16* base, int i, __amdgpu_buffer_rsrc_t (&r)[2])

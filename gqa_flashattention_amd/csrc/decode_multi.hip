@@ -131,8 +131,26 @@ __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_part
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const int L = min(p.kv_lens[b], p.max_kv_len);
   const int start = split * p.chunk;
+  // Paged: lanes j and 64 + j fetch the block-table entries of the split's
+  // logical pages lp0 + j and lp0 + 64 + j (at most 128 pages per split,
+  // checked on the host).  The split's first page follows from the split
+  // alone, so these loads are issued together with the sequence length's;
+  // entries past the table row are clamped to its last one, and those past
+  // the sequence are not used.
+  const int shift = p.page_shift;
+  const int lp0 = start >> shift;
+  int pt_raw[2] = {0, 0};
+  if constexpr (kPaged) {
+    const int32_t* trow = p.block_table + (size_t)b * p.max_pages;
+    const int j = threadIdx.x & 63;
+    pt_raw[0] = trow[min(lp0 + j, p.max_pages - 1)];
+    pt_raw[1] = trow[min(lp0 + 64 + j, p.max_pages - 1)];
+  }
+  const int L = min(p.kv_lens[b], p.max_kv_len);
+  // Keeps the table loads above the early exit below (the compiler would
+  // otherwise sink them there, behind the length's round trip).
+  if constexpr (kPaged) asm volatile("" : "+v"(pt_raw[0]), "+v"(pt_raw[1]));
   if (start >= L) return;
   const int end = min(start + p.chunk, L);
   const int nsteps = (end - start + S::kStep - 1) / S::kStep;
@@ -212,14 +230,11 @@ __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_part
   // Paged: lane j of pt[0] / pt[1] holds the physical page of the split's
   // logical page lp0 + j / lp0 + 64 + j (at most 128 pages per split,
   // checked on the host); entries are clamped into the pool.
-  const int shift = p.page_shift;
-  const int lp0 = start >> shift;
   int pt[2] = {0, 0};
   if constexpr (kPaged) {
     const int npg = ((end - 1) >> shift) - lp0 + 1;
-    const int32_t* trow = p.block_table + (size_t)b * p.max_pages + lp0;
-    if (lane < npg) pt[0] = min(max(trow[lane], 0), p.num_pages - 1);
-    if (lane + 64 < npg) pt[1] = min(max(trow[lane + 64], 0), p.num_pages - 1);
+    if (lane < npg) pt[0] = min(max(pt_raw[0], 0), p.num_pages - 1);
+    if (lane + 64 < npg) pt[1] = min(max(pt_raw[1], 0), p.num_pages - 1);
   }
   auto load_step = [&](auto slot_c, int s) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
