@@ -424,7 +424,9 @@ __device__ __forceinline__ void decode_partial_bf16(const DecodeParams& p) {
     };
     // One stream per wave.  The wave reads the K rows of a super-block of
     // kSblk blocks, then their V rows, then the next super-block's K rows,
-    // with two blocks' loads (16 KiB) in flight in two register slots.
+    // with two blocks' loads (16 KiB) in flight in two register slots: the
+    // K-before-V order of §5.6 opt2 (the scores read K first, the softmax
+    // and P.V read V later).
     // Measured on MI355X: a wave that streams K and V side by side (two
     // concurrent address streams) gets its bytes later than one that reads
     // them one after the other, and a super-block of two blocks is the
