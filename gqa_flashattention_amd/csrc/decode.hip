@@ -23,11 +23,12 @@
 //
 // A second kernel merges the partials: one wave per (sequence, query head)
 // and quarter of d, so a row's partials come in through four CUs' load
-// pipelines at once.  Merging inside the partial kernel -- the last workgroup to arrive
-// for a (sequence, KV head) merging the others' partials -- was measured
-// slower on MI355X: publishing partials across the 8 XCDs' separate L2s
-// costs either an L2 write-back per workgroup or agent-coherent accesses,
-// and the merge then runs serially on one CU at the end.
+// pipelines at once.  The one-launch form (decode_fused_bf16_kernel and the
+// fp32 split kernel with DecodeParams::counters set) merges inside the
+// split kernel instead -- the last workgroup to arrive for a (sequence, KV
+// head) merges the others' partials -- and is slower on MI355X: publishing
+// partials across the 8 XCDs' separate L2s costs agent-coherent stores and
+// an atomic per workgroup, and the merge then runs on one CU per head.
 
 #include <type_traits>
 
@@ -321,6 +322,7 @@ __device__ __forceinline__ void fused_merge_tail(const DecodeParams& p, int b, i
     __hip_atomic_store(p.counters + (size_t)b * p.H_kv + kvh, 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
+
 // The bf16 split sweep.  Grid: (n_split_max, H_kv, B); block: 256
 // threads.  kPaged: K/V live in a page pool addressed through the block
 // table (DecodeParams::block_table).  kFused: the one-launch decode
