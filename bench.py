@@ -118,6 +118,9 @@ def traffic_from_profiles(kernel: str, workload: str):
     return ent["bytes_per_launch"]
 
 
+GRAPH_KIND = ("the entry point's calls captured in one HIP graph and replayed (median replay / "
+              "calls); each replay checked bitwise against an eager call")
+
 TRAFFIC_SOURCE = ("profiles/all_workloads_kernel_stats_and_counters.md: calibrated rocprofv3 "
                   "FETCH_SIZE + WRITE_SIZE per launch, used only when that table was taken on the "
                   "kernel's current source (sha256 match); otherwise null")
@@ -166,6 +169,40 @@ def measure_copy_ceiling(reps=20):
 def _stats(ms_list):
     a = sorted(ms_list)
     return sum(a) / len(a), a[len(a) // 2]
+
+
+def graph_replay_us(call_at, n_calls, out, last_eager, replays=4):
+    """Per-call GPU time of `n_calls` calls captured in one HIP graph and
+    replayed: median replay time / n_calls, in us.  `call_at(i)` issues call
+    i on the current stream (it must allocate nothing).  Before each replay
+    `out` is cleared by an eager fill; after it, `out` must equal
+    `last_eager()` -- the eager result of the last captured call -- bit for
+    bit, or a RuntimeError is raised."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            for i in range(n_calls):
+                call_at(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gms = []
+    for r in range(replays):
+        out.zero_()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record()
+        g.replay()
+        gb.record()
+        torch.cuda.synchronize()
+        gms.append(ga.elapsed_time(gb))
+        want = last_eager()
+        torch.cuda.synchronize()
+        if not torch.equal(out, want):
+            raise RuntimeError(f"graph replay {r} differs from the eager call")
+    del g
+    return sorted(gms)[len(gms) // 2] * 1e3 / n_calls, len(gms)
 
 
 def time_decode_workload(name, steps, warmup):
@@ -226,44 +263,22 @@ def time_decode_workload(name, steps, warmup):
         # call through the binding), not by the GPU: replay `steps` calls
         # captured in one HIP graph to time the GPU side, after checking
         # that a replay reproduces the eager result bit for bit.
-        x0 = copies[0]
-        ref = out.clone()
-        gq.decode(x0["q"], x0["k"], x0["v"], x0["kv_lens"], max_kv_len=w.max_kv_len,
-                  scale=w.scale, out=ref, workspace=ws)
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g):
-                for i in range(steps):
-                    x = copies[i % ncopies]
-                    gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=w.max_kv_len,
-                              scale=w.scale, out=out, workspace=ws)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        gms = []
-        for r in range(4):
-            out.zero_()
-            ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ga.record()
-            g.replay()
-            gb.record()
-            torch.cuda.synchronize()
-            gms.append(ga.elapsed_time(gb))
+        def capture(i):
+            x = copies[i % ncopies]
+            gq.decode(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=w.max_kv_len,
+                      scale=w.scale, out=out, workspace=ws)
+
+        def last_eager():
             # The last captured call used copies[(steps - 1) % ncopies].
             last = copies[(steps - 1) % ncopies]
             want = torch.empty_like(out)
             gq.decode(last["q"], last["k"], last["v"], last["kv_lens"], max_kv_len=w.max_kv_len,
                       scale=w.scale, out=want, workspace=torch.empty_like(ws))
-            torch.cuda.synchronize()
-            if not torch.equal(out, want):
-                raise RuntimeError(f"{name}: graph replay {r} differs from the eager call")
-        graph = {"us_per_call": round(sorted(gms)[len(gms) // 2] * 1e3 / steps, 3),
-                 "calls_per_graph": steps, "replays": len(gms),
-                 "kind": "gqa_attn_decode calls captured in one HIP graph and replayed "
-                         "(median replay / calls); each replay checked bitwise against an "
-                         "eager call"}
-        del g
+            return want
+
+        g_us, reps = graph_replay_us(capture, steps, out, last_eager)
+        graph = {"us_per_call": round(g_us, 3), "calls_per_graph": steps, "replays": reps,
+                 "kind": GRAPH_KIND}
     gbs = w.decode_bytes() / (b2b_us * 1e-6) / 1e9
     part_bytes = w.kv_bytes() + w.B * w.H_q * w.T_q * w.d * w.elem_bytes
     part_gbs = part_bytes / (part_us * 1e-6) / 1e9
@@ -550,17 +565,21 @@ def main():
         gq.prefill(xp["q"], xp["k"], xp["v"], S_kv=wp.S_kv, causal=wp.causal,
                    causal_offset=wp.offset, scale=wp.scale, out=o_pre, stream=stream)
 
-    def decode_call(i, phase="both"):
+    def decode_call(i, phase="both", on=None, out=None, wsp=None):
+        # on=None: the timing stream; a graph capture passes the capturing one.
         x = copies[i % len(copies)]
+        st = stream if on is None else on
+        o = o_dec if out is None else out
+        w_ = ws if wsp is None else wsp
         if paged:
             gq.decode_paged(x["q"], x["k_pages"], x["v_pages"], x["block_table"], x["kv_lens"],
                             max_kv_len=wd.max_kv_len, scale=wd.scale, chunk_tokens=args.chunk,
-                            out=o_dec, workspace=ws, stream=stream, phase=phase)
+                            out=o, workspace=w_, stream=st, phase=phase)
             return
         fn = gq.decode_multi if multi else gq.decode
         fn(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=wd.max_kv_len,
-           scale=wd.scale, chunk_tokens=args.chunk, out=o_dec, workspace=ws,
-           stream=stream, phase=phase)
+           scale=wd.scale, chunk_tokens=args.chunk, out=o, workspace=w_,
+           stream=st, phase=phase)
 
     for i in range(args.warmup):
         if do_dec:
@@ -618,6 +637,19 @@ def main():
     step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
     dec_b2b_us = kd[0].elapsed_time(kd[1]) * 1e3 / K if do_dec else None
     part_us = kp[0].elapsed_time(kp[1]) * 1e3 / K if do_dec else None
+    # (4) The same K back-to-back decode calls captured in one HIP graph and
+    #     replayed (context beside `value`, which stays the eager rate).
+    dec_graph = None
+    if do_dec:
+        def last_eager():
+            want = torch.empty_like(o_dec)
+            decode_call(K - 1, out=want, wsp=torch.empty_like(ws))
+            return want
+        g_us, reps = graph_replay_us(lambda i: decode_call(i, on=torch.cuda.current_stream()),
+                                     K, o_dec, last_eager)
+        dec_graph = {"us_per_call": round(g_us, 3), "calls_per_graph": K, "replays": reps,
+                     "GB_s": round(wd.decode_bytes() / (g_us * 1e-6) / 1e9, 2),
+                     "kind": GRAPH_KIND}
     mean = lambda a: sum(a) / len(a)
     median = lambda a: sorted(a)[len(a) // 2]
 
@@ -664,7 +696,8 @@ def main():
                          "ms_median_in_step": round(median(dec_ms), 6),
                          "GB_s": round(gbs, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                          "bytes_per_call": wd.decode_bytes(),
-                         "partial_kernel_us_mean": round(part_us, 3)}
+                         "partial_kernel_us_mean": round(part_us, 3),
+                         "graph_replay": dec_graph}
         if fused_ok:
             f_us = kf[0].elapsed_time(kf[1]) * 1e3 / K
             out["decode"]["fused"] = {"entry_point": "gqa_attn_decode_fused",
