@@ -132,6 +132,36 @@ __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_part
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int start = split * p.chunk;
+
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  const int rg = wave % R;      // row group
+  const int kq = wave / R;      // key slot
+  const int c = lane & 31;      // row of this lane within the row group
+  const int h2 = lane >> 5;
+  const int t16 = lane & 15;
+  const int gamma = lane >> 4;
+
+  const int M = p.G * p.T_q;
+  const int row = 32 * rg + c;
+  const bool row_ok = row < M;
+  const size_t row0 = ((size_t)b * p.H_q + (size_t)kvh * p.G) * p.T_q;   // first folded row
+
+  // Q^T operand (B of S^T): row `row`, d = 16*kk + 8*h2 .. +8, through a
+  // buffer resource that ends at the M-th folded row, so that padding rows
+  // read as zeros without a branch.  These loads do not depend on the
+  // sequence length and are issued together with its load, so the two
+  // round trips overlap; a negative scale is applied exactly below by
+  // flipping Q's sign bits.
+  u32x4 qv[8];
+  {
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const __bf16*>(p.q) + row0 * kD), (short)0, (unsigned)M * kRowBytes, 0x00020000);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qv[kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, row * kRowBytes + 16 * h2 + 32 * kk, 0, 0);
+  }
   // Paged: lanes j and 64 + j fetch the block-table entries of the split's
   // logical pages lp0 + j and lp0 + 64 + j (at most 128 pages per split,
   // checked on the host).  The split's first page follows from the split
@@ -148,47 +178,30 @@ __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_part
     pt_raw[1] = trow[min(lp0 + 64 + j, p.max_pages - 1)];
   }
   const int L = min(p.kv_lens[b], p.max_kv_len);
-  // Keeps the table loads above the early exit below (the compiler would
-  // otherwise sink them there, behind the length's round trip).
+  // Keeps these loads above the early exit below (the compiler would
+  // otherwise sink them there, behind the length's round trip).  Q is
+  // complete from here on, before any of the ring's direct-to-LDS loads is
+  // issued: the compiler does not count those, so a later first use of Q
+  // would wait for them too.
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+v"(qv[kk]));
   if constexpr (kPaged) asm volatile("" : "+v"(pt_raw[0]), "+v"(pt_raw[1]));
   if (start >= L) return;
   const int end = min(start + p.chunk, L);
   const int nsteps = (end - start + S::kStep - 1) / S::kStep;
   // Steps [0, n_full) hold only keys every row sees (keys below L - T_q + 1).
   const int n_full = max(0, min(L - p.T_q + 1, end) - start) / S::kStep;
-
-  const int t = threadIdx.x;
-  const int wave = t >> 6;
-  const int lane = t & 63;
-  const int rg = wave % R;      // row group
-  const int kq = wave / R;      // key slot
-  const int c = lane & 31;      // row of this lane within the row group
-  const int h2 = lane >> 5;
-  const int t16 = lane & 15;
-  const int gamma = lane >> 4;
-
-  const int M = p.G * p.T_q;
-  const int row = 32 * rg + c;
-  const bool row_ok = row < M;
   // Last key this lane's row may see within the split (padding rows see all).
   const int vis_last = row_ok ? min(L - p.T_q + row % p.T_q, end - 1) : end - 1;
 
-  const size_t row0 = ((size_t)b * p.H_q + (size_t)kvh * p.G) * p.T_q;   // first folded row
   const __bf16* Kg = static_cast<const __bf16*>(p.k) + (kPaged ? 0 : ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD);
   const __bf16* Vg = static_cast<const __bf16*>(p.v) + (kPaged ? 0 : ((size_t)b * p.H_kv + kvh) * p.kv_cap * kD);
 
-  // Q^T operand (B of S^T): row `row`, d = 16*kk + 8*h2 .. +8.  A negative
-  // scale is applied exactly by flipping Q's sign bits.
   bf16x8 qb[8];
   {
-    const __bf16* qr = static_cast<const __bf16*>(p.q) + (row0 + (row_ok ? row : 0)) * kD + 8 * h2;
     const unsigned flip = p.q_negate ? 0x80008000u : 0u;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      u32x4 v = row_ok ? ld16(qr + 16 * kk) : u32x4{0, 0, 0, 0};
-      v ^= u32x4{flip, flip, flip, flip};
-      qb[kk] = as_bf16x8(v);
-    }
+    for (int kk = 0; kk < 8; ++kk) qb[kk] = as_bf16x8(qv[kk] ^ u32x4{flip, flip, flip, flip});
   }
 
   // Per-lane LDS addresses of the MFMA operands in ring slot 0 (other slots
