@@ -114,6 +114,36 @@ def test_decode_multi_t1_matches_decode():
     assert (lse[:, :, 0] - ld).abs().max().item() <= LSE_ATOL_BF16
 
 
+BELOW_BOUND = [
+    # (T_q, L, max_kv_len, chunk): one sequence shorter than the host bound,
+    # NaN-padded past L up to the capacity (4096)
+    (4, 1000, 4000, 128),     # the split holding L: its second step reaches past L
+    (4, 930, 4000, 128),      # ... its first step reaches past L, and is its only one
+    (4, 33, 4000, 0),         # one split holds the whole sequence; all others are empty
+    (4, 4000, 4000, 0),       # L equal to the bound
+    (3, 517, 3333, 256),      # 24 rows
+    (8, 700, 4000, 256),      # two row groups
+    (16, 2049, 4000, 0),      # four row groups
+]
+
+
+@pytest.mark.parametrize("case", BELOW_BOUND, ids=lambda c: f"T{c[0]}_L{c[1]}_max{c[2]}_c{c[3]}")
+def test_decode_multi_single_sequence_below_host_bound(case):
+    """A single sequence whose device length is below the host bound
+    max_kv_len: the grid covers the bound, so some splits hold keys past L
+    or none at all; every key past L must get weight zero (the NaN padding
+    there must not reach the output) and the empty splits must not count."""
+    T_q, L, max_len, chunk = case
+    w = _workload(1, 64, 8, T_q, (L,), 4096)
+    banner("decode_multi_below_bound", case)
+    x = inputs.make_decode_multi(w, device=DEV, seed=3000 + BELOW_BOUND.index(case))
+    o, lse = gq.decode_multi(x["q"], x["k"], x["v"], x["kv_lens"], max_kv_len=max_len,
+                             scale=w.scale, chunk_tokens=chunk, return_lse=True)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = _oracle(x, w)
+    _check(o, lse, ref_o, ref_lse, w, f"below bound {case}")
+
+
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.35])
 def test_decode_multi_scales(scale):
     """Negative (applied by flipping Q's sign), zero (uniform weights) and
