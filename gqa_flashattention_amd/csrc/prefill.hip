@@ -219,19 +219,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const __bf16* Kg = static_cast<const __bf16*>(p.k) + kv_base;
   const __bf16* Vg = static_cast<const __bf16*>(p.v) + kv_base;
 
-  // Q^T operand (B of S^T): query qrow, d = 16*ks + 8*h2 .. +8.  A negative
-  // scale is applied exactly by flipping Q's sign bits.
+  // Q^T operand (B of S^T): query qrow, d = 16*ks + 8*h2 .. +8, through a
+  // buffer resource over the wave's rows below S_q, so that rows past the
+  // chunk read as zeros without a branch (a branch per load made the
+  // compiler wait for the first loads before issuing the rest, and so
+  // before the tile loads).  A negative scale is applied exactly by flipping
+  // Q's sign bits, in a branch of its own so that the common case does not
+  // wait for Q before the tile loads are issued.
   bf16x8 qb[8];
   {
-    const bool ok = qrow < S_q;
-    const __bf16* qr =
-        static_cast<const __bf16*>(p.q) + (qrow0 + (size_t)(ok ? qrow : 0) * qstride) * kD + 8 * h2;
-    const unsigned flip = p.q_negate ? 0x80008000u : 0u;
+    const int nq = min(max(S_q - qw0, 0), 32);   // the wave's rows inside the chunk
+    // Wave-uniform by construction; readfirstlane says so to the compiler,
+    // which otherwise loops over the lanes' descriptors.
+    const uintptr_t qa =
+        reinterpret_cast<uintptr_t>(static_cast<const __bf16*>(p.q) + (qrow0 + (size_t)qw0 * qstride) * kD);
+    // (readfirstlane returns an int: each half goes through unsigned so
+    // that the low one is not sign-extended into the high one.)
+    const uintptr_t qau = ((uintptr_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)(qa >> 32)) << 32) |
+                          (uintptr_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)qa);
+    const unsigned bytes = __builtin_amdgcn_readfirstlane(
+        nq > 0 ? (unsigned)((nq - 1) * qstride + 1) * (kD * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(qau), (short)0, bytes, 0x00020000);
+    const int off = c * qstride * (kD * 2) + 16 * h2;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      u32x4 v = ok ? ld16(qr + 16 * ks) : u32x4{0, 0, 0, 0};
-      v ^= u32x4{flip, flip, flip, flip};
-      qb[ks] = as_bf16x8(v);
+    for (int ks = 0; ks < 8; ++ks)
+      qb[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rq, off + 32 * ks, 0, 0));
+    if (p.q_negate) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        u32x4 v = __builtin_bit_cast(u32x4, qb[ks]);
+        v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        qb[ks] = as_bf16x8(v);
+      }
     }
   }
 
