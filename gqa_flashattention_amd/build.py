@@ -32,6 +32,16 @@ DEVICE_FLAGS = [
 ]
 
 
+# Per-source flags.  decode.hip: kernel-argument preloading (gfx950 loads
+# the first kernel arguments into registers at wave launch; its kernels put
+# the values their first loads need first, so those loads do not wait for
+# the argument block).  Code built without it still runs: such a kernel
+# starts with a fallback that loads the preloaded arguments itself.
+SOURCE_FLAGS = {
+    "decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=5"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -41,7 +51,7 @@ def hipcc() -> str:
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *DEVICE_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c",
+    cmd = [hipcc(), *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-I", INCLUDE, "-I", CSRC, "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

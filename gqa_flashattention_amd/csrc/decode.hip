@@ -185,8 +185,20 @@ __device__ __forceinline__ void merge_fold(MergeAcc& st, MergeLoads<NG>& g, int 
 // round trip; splits past the sequence's count are discarded after the
 // loads.  NG (2, 4 or 8) follows the workspace's split count, so that a row
 // with few splits does not load the same partial several times.
+// What a merge's first load round needs.  The combine launch passes these
+// as kernel arguments of their own, ahead of DecodeParams, and this file is
+// built with kernel-argument preloading, so they arrive in registers with
+// the wave: the first loads issue without waiting for the argument block.
+struct CombineHead {
+  const int32_t* kv_lens;
+  const float* ws_o;
+  const float* ws_ml;
+  int n_split_max;
+  int rows_per_seq;   // H_q * T_q
+};
+
 template <typename OutT, int NG, int U>
-__device__ __forceinline__ void combine_rows(const DecodeParams& p, const int (&bh)[U],
+__device__ __forceinline__ void combine_rows(const DecodeParams& p, const CombineHead& hd, const int (&bh)[U],
                                              const int (&quarter)[U], int count, int lane) {
   // U (row, quarter) units, count of them valid: the first load round of
   // every unit is issued before any is folded, so the units share one
@@ -198,12 +210,15 @@ __device__ __forceinline__ void combine_rows(const DecodeParams& p, const int (&
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (u < count) {
-      const size_t part0 = (size_t)bh[u] * p.n_split_max;
-      len[u] = p.kv_lens[bh[u] / (p.H_q * p.T_q)];
-      merge_load(g[u], p.ws_ml + 2 * part0, p.ws_o + part0 * kD + 32 * quarter[u] + 4 * (lane & 7),
-                 slot, p.n_split_max, kCombSlots);
+      const size_t part0 = (size_t)bh[u] * hd.n_split_max;
+      len[u] = hd.kv_lens[bh[u] / hd.rows_per_seq];
+      merge_load(g[u], hd.ws_ml + 2 * part0, hd.ws_o + part0 * kD + 32 * quarter[u] + 4 * (lane & 7),
+                 slot, hd.n_split_max, kCombSlots);
     }
   }
+  // The first round's loads are issued before anything reads the other
+  // parameters (whose loads would otherwise go first and be waited for).
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (u >= count) break;
@@ -245,9 +260,10 @@ __device__ __forceinline__ void combine_rows(const DecodeParams& p, const int (&
 }
 
 template <typename OutT, int NG>
-__device__ __forceinline__ void combine_row(const DecodeParams& p, int bh, int quarter, int lane) {
+__device__ __forceinline__ void combine_row(const DecodeParams& p, const CombineHead& hd, int bh, int quarter,
+                                            int lane) {
   const int bhs[1] = {bh}, qs[1] = {quarter};
-  combine_rows<OutT, NG, 1>(p, bhs, qs, 1, lane);
+  combine_rows<OutT, NG, 1>(p, hd, bhs, qs, 1, lane);
 }
 
 // Splits per lane and load round of the merge for a workspace of
@@ -301,6 +317,7 @@ __device__ __forceinline__ void fused_merge_tail(const DecodeParams& p, int b, i
   // Wave w takes units w, w + nwaves, ... in batches whose first load
   // rounds are all in flight together (at most ~96 registers of loads).
   const int ng = combine_ng(p.n_split_max);
+  const CombineHead hd{p.kv_lens, p.ws_o, p.ws_ml, p.n_split_max, p.H_q * p.T_q};
   auto run = [&](auto ngc, auto uc) {
     constexpr int NG = decltype(ngc)::value, U = decltype(uc)::value;
     for (int base = wave; base < 4 * M; base += nwaves * U) {
@@ -312,7 +329,7 @@ __device__ __forceinline__ void fused_merge_tail(const DecodeParams& p, int b, i
         qs[i] = u & 3;
         count += base + nwaves * i < 4 * M;
       }
-      combine_rows<OutT, NG, U>(p, bhs, qs, count, lane);
+      combine_rows<OutT, NG, U>(p, hd, bhs, qs, count, lane);
     }
   };
   if (ng == 2) run(std::integral_constant<int, 2>(), std::integral_constant<int, 8>());
@@ -328,7 +345,7 @@ __device__ __forceinline__ void fused_merge_tail(const DecodeParams& p, int b, i
 // table (DecodeParams::block_table).  kFused: the one-launch decode
 // (DecodeParams::counters set) merges the partials at the end.
 template <bool kPaged, bool kFused>
-__device__ __forceinline__ void decode_partial_bf16(const DecodeParams& p) {
+__device__ __forceinline__ void decode_partial_bf16(const DecodeParams& p, int kv_len) {
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
@@ -346,7 +363,7 @@ __device__ __forceinline__ void decode_partial_bf16(const DecodeParams& p) {
   int pt_raw = 0;
   if constexpr (kPaged)
     pt_raw = p.block_table[(size_t)b * p.max_pages + min(lp0 + lane, p.max_pages - 1)];
-  const int L = min(p.kv_lens[b], p.max_kv_len);
+  const int L = min(kv_len, p.max_kv_len);
   // Keeps the table load above the early exit below (the compiler would
   // otherwise sink it there, behind the length's round trip).
   if constexpr (kPaged) asm volatile("" : "+v"(pt_raw));
@@ -618,15 +635,20 @@ __device__ __forceinline__ void decode_partial_bf16(const DecodeParams& p) {
 
 // The two-launch split kernel fits three waves per SIMD (at most 168
 // registers); the one-launch kernel, whose merge tail needs more registers,
-// is a kernel of its own at two waves per SIMD.
+// is a kernel of its own at two waves per SIMD.  The split kernel takes the
+// sequence lengths as its first argument, preloaded into registers (see
+// CombineHead): the length load is issued first, together with the loads
+// of the other parameters, instead of after them.
 template <bool kPaged>
-__global__ __launch_bounds__(256, 3) void decode_partial_bf16_kernel(DecodeParams p) {
-  decode_partial_bf16<kPaged, false>(p);
+__global__ __launch_bounds__(256, 3) void decode_partial_bf16_kernel(const int32_t* kv_lens, DecodeParams p) {
+  const int kv_len = kv_lens[blockIdx.z];
+  __builtin_amdgcn_sched_barrier(0);
+  decode_partial_bf16<kPaged, false>(p, kv_len);
 }
 
 template <bool kPaged>
 __global__ __launch_bounds__(256, 2) void decode_fused_bf16_kernel(DecodeParams p) {
-  decode_partial_bf16<kPaged, true>(p);
+  decode_partial_bf16<kPaged, true>(p, p.kv_lens[blockIdx.z]);
 }
 
 // fp32 decode partial: one workgroup of 256 threads per 64-key split.  The
@@ -761,10 +783,14 @@ __global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p)
 }
 
 
-// The combine launch: one wave per (folded row, quarter of d).
+// The combine launch: one wave per (folded row, quarter of d); the values
+// its first load round needs come first, preloaded (see CombineHead).
 template <typename OutT, int NG>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
-  combine_row<OutT, NG>(p, blockIdx.x, blockIdx.y, threadIdx.x);
+__global__ __launch_bounds__(64) void decode_combine_kernel(const int32_t* kv_lens, const float* ws_o,
+                                                            const float* ws_ml, int n_split_max, int rows_per_seq,
+                                                            DecodeParams p) {
+  const CombineHead hd{kv_lens, ws_o, ws_ml, n_split_max, rows_per_seq};
+  combine_row<OutT, NG>(p, hd, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, int phases) {
@@ -775,11 +801,11 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, i
       if (paged && fused)
         hipLaunchKernelGGL(decode_fused_bf16_kernel<true>, grid, dim3(256), 0, stream, p);
       else if (paged)
-        hipLaunchKernelGGL(decode_partial_bf16_kernel<true>, grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(decode_partial_bf16_kernel<true>, grid, dim3(256), 0, stream, p.kv_lens, p);
       else if (fused)
         hipLaunchKernelGGL(decode_fused_bf16_kernel<false>, grid, dim3(256), 0, stream, p);
       else
-        hipLaunchKernelGGL(decode_partial_bf16_kernel<false>, grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(decode_partial_bf16_kernel<false>, grid, dim3(256), 0, stream, p.kv_lens, p);
     } else {
       switch ((p.G + 3) / 4) {
         case 1: hipLaunchKernelGGL(decode_partial_f32_kernel<1>, grid, dim3(256), 0, stream, p); break;
@@ -795,16 +821,18 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, i
   if ((phases & kDecodeCombine) && p.counters == nullptr) {
     const dim3 grid(p.B * p.H_q * p.T_q, 4);
     const int ng = combine_ng(p.n_split_max);
+#define COMBINE_ARGS p.kv_lens, p.ws_o, p.ws_ml, p.n_split_max, p.H_q * p.T_q, p
     if (bf16) {
-      if (ng == 2) hipLaunchKernelGGL((decode_combine_kernel<__bf16, 2>), grid, dim3(64), 0, stream, p);
-      else if (ng == 4) hipLaunchKernelGGL((decode_combine_kernel<__bf16, 4>), grid, dim3(64), 0, stream, p);
-      else hipLaunchKernelGGL((decode_combine_kernel<__bf16, 8>), grid, dim3(64), 0, stream, p);
+      if (ng == 2) hipLaunchKernelGGL((decode_combine_kernel<__bf16, 2>), grid, dim3(64), 0, stream, COMBINE_ARGS);
+      else if (ng == 4) hipLaunchKernelGGL((decode_combine_kernel<__bf16, 4>), grid, dim3(64), 0, stream, COMBINE_ARGS);
+      else hipLaunchKernelGGL((decode_combine_kernel<__bf16, 8>), grid, dim3(64), 0, stream, COMBINE_ARGS);
     } else {
-      if (ng == 2) hipLaunchKernelGGL((decode_combine_kernel<float, 2>), grid, dim3(64), 0, stream, p);
-      else if (ng == 4) hipLaunchKernelGGL((decode_combine_kernel<float, 4>), grid, dim3(64), 0, stream, p);
-      else hipLaunchKernelGGL((decode_combine_kernel<float, 8>), grid, dim3(64), 0, stream, p);
+      if (ng == 2) hipLaunchKernelGGL((decode_combine_kernel<float, 2>), grid, dim3(64), 0, stream, COMBINE_ARGS);
+      else if (ng == 4) hipLaunchKernelGGL((decode_combine_kernel<float, 4>), grid, dim3(64), 0, stream, COMBINE_ARGS);
+      else hipLaunchKernelGGL((decode_combine_kernel<float, 8>), grid, dim3(64), 0, stream, COMBINE_ARGS);
     }
   }
+#undef COMBINE_ARGS
   return hipGetLastError();
 }
 

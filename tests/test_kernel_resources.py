@@ -27,8 +27,8 @@ ALLOWED_SCRATCH = {}
 def test_no_scratch(src, tmp_path):
     if src == "api.hip":
         pytest.skip("host code only")
-    cmd = [build.hipcc(), *build.DEVICE_FLAGS, "-I", build.INCLUDE, "-I", build.CSRC,
-           "--cuda-device-only", "-S", os.path.join(build.CSRC, src), "-o",
+    cmd = [build.hipcc(), *build.DEVICE_FLAGS, *build.SOURCE_FLAGS.get(src, []), "-I", build.INCLUDE,
+           "-I", build.CSRC, "--cuda-device-only", "-S", os.path.join(build.CSRC, src), "-o",
            str(tmp_path / "out.s"), "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -49,8 +49,8 @@ def test_m0_only_in_lds_dma_sequences(src, tmp_path):
     other use would mean the compiler keeps a value of its own in M0 that
     the sequence could overwrite."""
     out = tmp_path / "out.s"
-    cmd = [build.hipcc(), *build.DEVICE_FLAGS, "-I", build.INCLUDE, "-I", build.CSRC,
-           "--cuda-device-only", "-S", os.path.join(build.CSRC, src), "-o", str(out)]
+    cmd = [build.hipcc(), *build.DEVICE_FLAGS, *build.SOURCE_FLAGS.get(src, []), "-I", build.INCLUDE,
+           "-I", build.CSRC, "--cuda-device-only", "-S", os.path.join(build.CSRC, src), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln.split(";")[0].strip() for ln in out.read_text().splitlines()]
@@ -65,3 +65,23 @@ def test_m0_only_in_lds_dma_sequences(src, tmp_path):
         if not ok:
             bad.append((i, ln))
     assert not bad, f"M0 used outside the LDS DMA sequences: {bad[:5]}"
+
+
+def test_decode_leading_arguments_preloaded(tmp_path):
+    """The decode split kernel and the combine kernel take the values their
+    first loads need as leading kernel arguments; the build preloads them
+    into registers (and keeps the kernels' other arguments in memory)."""
+    out = tmp_path / "out.s"
+    cmd = [build.hipcc(), *build.DEVICE_FLAGS, *build.SOURCE_FLAGS.get("decode.hip", []), "-I",
+           build.INCLUDE, "-I", build.CSRC, "--cuda-device-only", "-S",
+           os.path.join(build.CSRC, "decode.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    text = out.read_text()
+    found = dict(re.findall(r"\.amdhsa_kernel (\S+)\n(?:.*\n)*?\s*\.amdhsa_user_sgpr_kernarg_preload_length (\d+)",
+                            text))
+    split = [n for n in found if "decode_partial_bf16_kernel" in n]
+    comb = [n for n in found if "decode_combine_kernel" in n]
+    assert len(split) == 2 and len(comb) == 6, found
+    assert all(int(found[n]) == 2 for n in split), found        # the length pointer
+    assert all(int(found[n]) == 8 for n in comb), found         # 3 pointers, 2 ints
