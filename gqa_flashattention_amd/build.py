@@ -32,13 +32,15 @@ DEVICE_FLAGS = [
 ]
 
 
-# Per-source flags.  decode.hip: kernel-argument preloading (gfx950 loads
-# the first kernel arguments into registers at wave launch; its kernels put
-# the values their first loads need first, so those loads do not wait for
-# the argument block).  Code built without it still runs: such a kernel
-# starts with a fallback that loads the preloaded arguments itself.
+# Per-source flags.  decode.hip, decode_multi.hip: kernel-argument
+# preloading (gfx950 loads the first kernel arguments into registers at wave
+# launch; these files' kernels put the values their first loads need first,
+# so those loads do not wait for the argument block).  Where the firmware
+# does not preload, a kernel starts with a fallback that loads those
+# arguments itself.
 SOURCE_FLAGS = {
     "decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=5"],
+    "decode_multi.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"],
 }
 
 

@@ -120,10 +120,14 @@ constexpr int kRedFloats = 32 * kRedStride;
 }  // namespace
 
 // Grid: (n_split_max, H_kv, B); block: 64 * W threads.  kPaged: K/V live in
-// a page pool addressed through the block table.
+// a page pool addressed through the block table.  What the first loads
+// need (the sequence lengths, Q, H_kv and the fold's M = G * T_q rows) comes
+// as leading kernel arguments, which this file's build preloads into
+// registers: the length and Q loads issue at wave start, before the
+// argument block has arrived.
 template <int R, bool kPaged>
 __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_partial_kernel(
-    DecodeParams p) {
+    const int32_t* kv_lens, const __bf16* q, int H_kv, int M, DecodeParams p) {
   using S = typename MqLaunch<R>::S;
   // K ring then V ring, contiguous so that the merge can reuse both.
   __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][S::kRing][S::kStep * kD];
@@ -131,7 +135,6 @@ __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_part
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const int start = split * p.chunk;
 
   const int t = threadIdx.x;
   const int wave = t >> 6;
@@ -143,10 +146,9 @@ __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_part
   const int t16 = lane & 15;
   const int gamma = lane >> 4;
 
-  const int M = p.G * p.T_q;
   const int row = 32 * rg + c;
   const bool row_ok = row < M;
-  const size_t row0 = ((size_t)b * p.H_q + (size_t)kvh * p.G) * p.T_q;   // first folded row
+  const size_t row0 = ((size_t)b * H_kv + kvh) * M;   // first folded row: (b*H_q + kvh*G)*T_q
 
   // Q^T operand (B of S^T): row `row`, d = 16*kk + 8*h2 .. +8, through a
   // buffer resource that ends at the M-th folded row, so that padding rows
@@ -154,14 +156,18 @@ __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_part
   // sequence length and are issued together with its load, so the two
   // round trips overlap; a negative scale is applied exactly below by
   // flipping Q's sign bits.
+  const int kv_len = kv_lens[b];
   u32x4 qv[8];
   {
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(static_cast<const __bf16*>(p.q) + row0 * kD), (short)0, (unsigned)M * kRowBytes, 0x00020000);
+        (void*)(q + row0 * kD), (short)0, (unsigned)M * kRowBytes, 0x00020000);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       qv[kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, row * kRowBytes + 16 * h2 + 32 * kk, 0, 0);
   }
+  // Nothing that reads the argument block is scheduled above these loads.
+  __builtin_amdgcn_sched_barrier(0);
+  const int start = split * p.chunk;
   // Paged: lanes j and 64 + j fetch the block-table entries of the split's
   // logical pages lp0 + j and lp0 + 64 + j (at most 128 pages per split,
   // checked on the host).  The split's first page follows from the split
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(MqLaunch<R>::S::kThreads, 1) void decode_multi_part
     pt_raw[0] = trow[min(lp0 + j, p.max_pages - 1)];
     pt_raw[1] = trow[min(lp0 + 64 + j, p.max_pages - 1)];
   }
-  const int L = min(p.kv_lens[b], p.max_kv_len);
+  const int L = min(kv_len, p.max_kv_len);
   // Keeps these loads above the early exit below (the compiler would
   // otherwise sink them there, behind the length's round trip).  Q is
   // complete from here on, before any of the ring's direct-to-LDS loads is
@@ -539,26 +545,34 @@ hipError_t launch_decode_multi(const DecodeParams& p, hipStream_t stream, int ph
   if (phases & kDecodePartial) {
     const dim3 grid(p.n_split_max, p.H_kv, p.B);
     const bool paged = p.block_table != nullptr;
+#define MULTI_ARGS p.kv_lens, static_cast<const __bf16*>(p.q), p.H_kv, p.G * p.T_q, p
     switch (decode_multi_row_groups(p.G * p.T_q)) {
       case 1:
         if (paged)
-          hipLaunchKernelGGL((decode_multi_partial_kernel<1, true>), grid, dim3(MqLaunch<1>::S::kThreads), 0, stream, p);
+          hipLaunchKernelGGL((decode_multi_partial_kernel<1, true>), grid, dim3(MqLaunch<1>::S::kThreads), 0, stream,
+                             MULTI_ARGS);
         else
-          hipLaunchKernelGGL((decode_multi_partial_kernel<1, false>), grid, dim3(MqLaunch<1>::S::kThreads), 0, stream, p);
+          hipLaunchKernelGGL((decode_multi_partial_kernel<1, false>), grid, dim3(MqLaunch<1>::S::kThreads), 0, stream,
+                             MULTI_ARGS);
         break;
       case 2:
         if (paged)
-          hipLaunchKernelGGL((decode_multi_partial_kernel<2, true>), grid, dim3(MqLaunch<2>::S::kThreads), 0, stream, p);
+          hipLaunchKernelGGL((decode_multi_partial_kernel<2, true>), grid, dim3(MqLaunch<2>::S::kThreads), 0, stream,
+                             MULTI_ARGS);
         else
-          hipLaunchKernelGGL((decode_multi_partial_kernel<2, false>), grid, dim3(MqLaunch<2>::S::kThreads), 0, stream, p);
+          hipLaunchKernelGGL((decode_multi_partial_kernel<2, false>), grid, dim3(MqLaunch<2>::S::kThreads), 0, stream,
+                             MULTI_ARGS);
         break;
       default:
         if (paged)
-          hipLaunchKernelGGL((decode_multi_partial_kernel<4, true>), grid, dim3(MqLaunch<4>::S::kThreads), 0, stream, p);
+          hipLaunchKernelGGL((decode_multi_partial_kernel<4, true>), grid, dim3(MqLaunch<4>::S::kThreads), 0, stream,
+                             MULTI_ARGS);
         else
-          hipLaunchKernelGGL((decode_multi_partial_kernel<4, false>), grid, dim3(MqLaunch<4>::S::kThreads), 0, stream, p);
+          hipLaunchKernelGGL((decode_multi_partial_kernel<4, false>), grid, dim3(MqLaunch<4>::S::kThreads), 0, stream,
+                             MULTI_ARGS);
         break;
     }
+#undef MULTI_ARGS
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -85,3 +85,18 @@ def test_decode_leading_arguments_preloaded(tmp_path):
     assert len(split) == 2 and len(comb) == 6, found
     assert all(int(found[n]) == 2 for n in split), found        # the length pointer
     assert all(int(found[n]) == 8 for n in comb), found         # 3 pointers, 2 ints
+
+
+def test_multi_token_leading_arguments_preloaded(tmp_path):
+    """The multi-token split kernel's leading arguments (the length pointer,
+    Q, H_kv and the fold's rows) are preloaded into registers."""
+    out = tmp_path / "out.s"
+    cmd = [build.hipcc(), *build.DEVICE_FLAGS, *build.SOURCE_FLAGS.get("decode_multi.hip", []), "-I",
+           build.INCLUDE, "-I", build.CSRC, "--cuda-device-only", "-S",
+           os.path.join(build.CSRC, "decode_multi.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    found = dict(re.findall(r"\.amdhsa_kernel (\S+)\n(?:.*\n)*?\s*\.amdhsa_user_sgpr_kernarg_preload_length (\d+)",
+                            out.read_text()))
+    multi = [n for n in found if "decode_multi_partial_kernel" in n]
+    assert len(multi) == 6 and all(int(found[n]) == 6 for n in multi), found
