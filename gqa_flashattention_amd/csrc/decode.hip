@@ -661,11 +661,14 @@ constexpr int kF32Chunk = 64;
 // QS = ceil(G / 4): query slots per thread in the score phase (2*QS in P.V),
 // so that no thread computes rows past the group's G heads.
 template <int QS>
-__global__ __launch_bounds__(256) void decode_partial_f32_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) void decode_partial_f32_kernel(const int32_t* kv_lens, DecodeParams p) {
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const int L = min(p.kv_lens[b], p.max_kv_len);
+  // The sequence lengths come first, preloaded (as for the bf16 kernel).
+  const int kv_len = kv_lens[b];
+  __builtin_amdgcn_sched_barrier(0);
+  const int L = min(kv_len, p.max_kv_len);
   const int start = split * kF32Chunk;
   if (start >= L) return;
   const int cnt = min(kF32Chunk, L - start);
@@ -808,10 +811,10 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t stream, i
         hipLaunchKernelGGL(decode_partial_bf16_kernel<false>, grid, dim3(256), 0, stream, p.kv_lens, p);
     } else {
       switch ((p.G + 3) / 4) {
-        case 1: hipLaunchKernelGGL(decode_partial_f32_kernel<1>, grid, dim3(256), 0, stream, p); break;
-        case 2: hipLaunchKernelGGL(decode_partial_f32_kernel<2>, grid, dim3(256), 0, stream, p); break;
-        case 3: hipLaunchKernelGGL(decode_partial_f32_kernel<3>, grid, dim3(256), 0, stream, p); break;
-        default: hipLaunchKernelGGL(decode_partial_f32_kernel<4>, grid, dim3(256), 0, stream, p); break;
+        case 1: hipLaunchKernelGGL(decode_partial_f32_kernel<1>, grid, dim3(256), 0, stream, p.kv_lens, p); break;
+        case 2: hipLaunchKernelGGL(decode_partial_f32_kernel<2>, grid, dim3(256), 0, stream, p.kv_lens, p); break;
+        case 3: hipLaunchKernelGGL(decode_partial_f32_kernel<3>, grid, dim3(256), 0, stream, p.kv_lens, p); break;
+        default: hipLaunchKernelGGL(decode_partial_f32_kernel<4>, grid, dim3(256), 0, stream, p.kv_lens, p); break;
       }
     }
     hipError_t e = hipGetLastError();

@@ -68,9 +68,9 @@ def test_m0_only_in_lds_dma_sequences(src, tmp_path):
 
 
 def test_decode_leading_arguments_preloaded(tmp_path):
-    """The decode split kernel and the combine kernel take the values their
-    first loads need as leading kernel arguments; the build preloads them
-    into registers (and keeps the kernels' other arguments in memory)."""
+    """The decode split kernels (bf16 and fp32) and the combine kernel take
+    the values their first loads need as leading kernel arguments; the build
+    preloads them into registers (and keeps the other arguments in memory)."""
     out = tmp_path / "out.s"
     cmd = [build.hipcc(), *build.DEVICE_FLAGS, *build.SOURCE_FLAGS.get("decode.hip", []), "-I",
            build.INCLUDE, "-I", build.CSRC, "--cuda-device-only", "-S",
@@ -80,9 +80,9 @@ def test_decode_leading_arguments_preloaded(tmp_path):
     text = out.read_text()
     found = dict(re.findall(r"\.amdhsa_kernel (\S+)\n(?:.*\n)*?\s*\.amdhsa_user_sgpr_kernarg_preload_length (\d+)",
                             text))
-    split = [n for n in found if "decode_partial_bf16_kernel" in n]
+    split = [n for n in found if "decode_partial_bf16_kernel" in n or "decode_partial_f32_kernel" in n]
     comb = [n for n in found if "decode_combine_kernel" in n]
-    assert len(split) == 2 and len(comb) == 6, found
+    assert len(split) == 6 and len(comb) == 6, found
     assert all(int(found[n]) == 2 for n in split), found        # the length pointer
     assert all(int(found[n]) == 8 for n in comb), found         # 3 pointers, 2 ints
 
