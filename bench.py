@@ -96,14 +96,43 @@ def calibrate_copy():
           flush=True)
 
 
+def source_digest(path: str) -> str:
+    """First 16 hex digits of the sha256 of a C++/HIP source's code: `//`
+    comments (outside string literals) and whitespace removed, so that a
+    comment edit leaves it unchanged and any code edit changes it."""
+    out, i, text = [], 0, open(path, encoding="utf-8").read()
+    in_str = False
+    while i < len(text):
+        ch = text[i]
+        if in_str:
+            out.append(ch)
+            if ch == "\\":
+                out.append(text[i + 1:i + 2])
+                i += 2
+                continue
+            if ch == '"':
+                in_str = False
+        elif ch == '"':
+            in_str = True
+            out.append(ch)
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = len(text) if j < 0 else j
+            continue
+        elif not ch.isspace():
+            out.append(ch)
+        i += 1
+    import hashlib
+    return hashlib.sha256("".join(out).encode()).hexdigest()[:16]
+
+
 def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` on `workload` from the committed
     counter summary (calibrated FETCH_SIZE + WRITE_SIZE), if it was taken on
-    the current kernel source; otherwise None."""
+    the current kernel source (same code digest); otherwise None."""
     path = os.path.join(ROOT, "profiles", "all_workloads_kernel_stats_and_counters.md")
     if not os.path.exists(path):
         return None
-    import hashlib
     text = open(path).read()
     m = re.search(r"```json\n(.*?)\n```", text, re.S)
     if not m:
@@ -112,8 +141,7 @@ def traffic_from_profiles(kernel: str, workload: str):
     if not ent:
         return None
     src = os.path.join(ROOT, "gqa_flashattention_amd", "csrc", ent["source"])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if sha != ent.get("source_sha256_16"):
+    if source_digest(src) != ent.get("source_code_sha256_16"):
         return None
     return ent["bytes_per_launch"]
 
@@ -123,7 +151,8 @@ GRAPH_KIND = ("the entry point's calls captured in one HIP graph and replayed (m
 
 TRAFFIC_SOURCE = ("profiles/all_workloads_kernel_stats_and_counters.md: calibrated rocprofv3 "
                   "FETCH_SIZE + WRITE_SIZE per launch, used only when that table was taken on the "
-                  "kernel's current source (sha256 match); otherwise null")
+                  "kernel's current source (sha256 of its code, comments and whitespace removed); "
+                  "otherwise null")
 
 
 def measure_copy_ceiling(reps=20):

@@ -174,17 +174,6 @@ __device__ __forceinline__ void merge_fold(MergeAcc& st, MergeLoads<NG>& g, int 
   st.M = gm;
 }
 
-// Combine: one wave per (output row, quarter of d), rows being (sequence,
-// query head, token); the 4 waves of a row run on different CUs, so a row's
-// partials are fetched by four load pipelines at once.  Lane l takes split
-// slot j = l / 8 (splits j, j + 8, j + 16, ...) and output columns
-// 32*quarter + 4*(l % 8) .. +4; the 8 slots then merge across lanes
-// (xor 8, 16, 32).  Normalises once and rounds to the output dtype (the
-// final O / l of §4).  The first 8*NG splits' loads are issued together with
-// the sequence length's, so a call of up to 8*NG splits costs one memory
-// round trip; splits past the sequence's count are discarded after the
-// loads.  NG (2, 4 or 8) follows the workspace's split count, so that a row
-// with few splits does not load the same partial several times.
 // What a merge's first load round needs.  The combine launch passes these
 // as kernel arguments of their own, ahead of DecodeParams, and this file is
 // built with kernel-argument preloading, so they arrive in registers with
@@ -197,6 +186,17 @@ struct CombineHead {
   int rows_per_seq;   // H_q * T_q
 };
 
+// Combine: one wave per (output row, quarter of d), rows being (sequence,
+// query head, token); the 4 waves of a row run on different CUs, so a row's
+// partials are fetched by four load pipelines at once.  Lane l takes split
+// slot j = l / 8 (splits j, j + 8, j + 16, ...) and output columns
+// 32*quarter + 4*(l % 8) .. +4; the 8 slots then merge across lanes
+// (xor 8, 16, 32).  Normalises once and rounds to the output dtype (the
+// final O / l of §4).  The first 8*NG splits' loads are issued together with
+// the sequence length's, so a call of up to 8*NG splits costs one memory
+// round trip; splits past the sequence's count are discarded after the
+// loads.  NG (2, 4 or 8) follows the workspace's split count, so that a row
+// with few splits does not load the same partial several times.
 template <typename OutT, int NG, int U>
 __device__ __forceinline__ void combine_rows(const DecodeParams& p, const CombineHead& hd, const int (&bh)[U],
                                              const int (&quarter)[U], int count, int lane) {

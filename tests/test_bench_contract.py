@@ -29,6 +29,22 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout.strip() == ""
 
 
+def test_source_digest_follows_code_not_comments(tmp_path):
+    """roofline.traffic is reused only while the kernel's code is unchanged:
+    the digest ignores `//` comments and whitespace, not code or string
+    contents (a `//` inside a string literal is code)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    a, b, c, d = (tmp_path / n for n in ("a.hip", "b.hip", "c.hip", "d.hip"))
+    a.write_text('int x = 1;  // one\n  asm("s_nop // a \\" b");\n')
+    b.write_text('// header\nint x = 1;\nasm("s_nop // a \\" b"); // trailing\n')
+    c.write_text('int x = 2;\nasm("s_nop // a \\" b");\n')
+    d.write_text('int x = 1;\nasm("s_nop // A \\" b");\n')
+    assert bench.source_digest(str(a)) == bench.source_digest(str(b))
+    assert bench.source_digest(str(a)) != bench.source_digest(str(c))
+    assert bench.source_digest(str(a)) != bench.source_digest(str(d))
+
+
 @pytest.mark.gpu
 def test_short_bench_prints_one_contract_line():
     r = subprocess.run([sys.executable, "-u", BENCH, "--steps", "4", "--warmup", "2",
