@@ -474,14 +474,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // softmax of tile j (P = exp2(S*scale - ref), rounded to bf16; fp32 row
   // sums) spread between them so that the matrix unit and the vector ALUs
   // work at the same time.  Order: the 16 MFMAs of P.V(j-1), then S(j+1)
-  // rows 0-31 (reusing the registers of S(j) rows 0-31), then rows 32-63.
-  // The 32 exponentials of S(j) are spread evenly over the first 24 slots
-  // (two, one, one per slot): rows 0-31 finish by slot 11 and rows 32-63
-  // by slot 23, just before their registers are overwritten.  Two waves
-  // share a SIMD and run the same sequence in step, so spreading the
-  // exponentials keeps the vector port's load per slot near one MFMA's
-  // duration instead of doubling it for half of the sequence.  Returns
-  // this lane's fp32 sum of P(j).
+  // rows 0-31 (reusing the registers of S(j) rows 0-31), then rows 32-63
+  // (in the registers of P(j-1), free once the P.V MFMAs have read it).
+  // Exponential k of S(j) runs in slot k, one per MFMA: rows 0-31 finish
+  // by slot 15, before their registers are overwritten, and rows 32-63
+  // stay live to the end of the sequence.  Two waves share a SIMD and run
+  // the same sequence in step, so an even spread keeps the vector port's
+  // load per slot below one MFMA's duration.  Returns this lane's fp32 sum
+  // of P(j).
   // `ld` (when not null) lists two tile loads as {kv, buffer, tile, page}
   // entries; their four instructions are spread over the sequence (one
   // every eighth MFMA) so that the load path is fed gradually instead of
@@ -528,10 +528,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
                                                           0, 0, 0);
       }
       // Exponential k (score k of the lane: rows 32*(k/16).., key 32*(k/16)
-      // + 8*((k%16)/4... as S.s[k/16][k%16]) runs in slot 3k/4.
+      // + 8*((k%16)/4... as S.s[k/16][k%16]) runs in slot k.
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
-        if ((3 * k) / 4 != i) continue;
+        if (k != i) continue;
         ev[k] = fast_exp2(__builtin_fmaf(T.s[k >> 4][k & 15], sl2, negr));
         if ((k & 1) == 0) {
           // Keep this exponential in this slot (not sunk towards its use).
