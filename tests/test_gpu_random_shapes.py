@@ -94,15 +94,31 @@ def _varlen_cases(n):
     return out
 
 
+def _paged_decode_cases(n):
+    out = []
+    for _ in range(n):
+        T_q = int(_pick([1, 1, 2, 4, 8, 16]))
+        H_kv = int(_pick([1, 2, 4, 8]))
+        gs = [g for g in (1, 2, 4, 8) if g * T_q <= 128 and g * H_kv <= 64]
+        G = int(_pick(gs))
+        B = int(_rng.randint(1, 4))
+        lens = tuple(int(x) for x in _rng.randint(T_q, 3000, size=B))
+        cap = max(lens) + int(_rng.randint(0, 100))
+        out.append((B, G * H_kv, H_kv, T_q, lens, cap, int(_pick([16, 32, 64, 128, 256]))))
+    return out
+
+
 DECODE_BF16 = _decode_cases(10, "bf16", 4000, [0, 128, 256, 384, 512, 768, 1024])
 DECODE_F32 = _decode_cases(4, "f32", 2000, [0, 64])
 MULTI = _multi_cases(8)
 PREFILL = _prefill_cases(8)
 VARLEN = _varlen_cases(4)
+PAGED_DECODE = _paged_decode_cases(6)
+PAGED_PREFILL = [c + (int(_pick([16, 32, 64, 128])),) for c in _varlen_cases(3)]
 
 
 def _id(c):
-    return "_".join(str(x).replace(" ", "").replace(",", "-").strip("()") for x in c)
+    return "_".join("-".join(map(str, x)) if isinstance(x, tuple) else str(x) for x in c)
 
 
 @pytest.mark.parametrize("case", DECODE_BF16 + DECODE_F32, ids=_id)
@@ -173,6 +189,48 @@ def test_random_prefill_varlen(case):
     ro, rl = oracle.prefill_varlen(np32(x["q"]), np32(x["k"]), np32(x["v"]),
                                    x["cu_seqlens_q"].cpu().numpy(), np.array(lens), w.scale,
                                    causal=causal)
+    cu = x["cu_seqlens_q"].cpu().tolist()
+    for b in range(len(q_lens)):
+        if cu[b + 1] == cu[b]:
+            continue
+        check_bf16(np32(o[cu[b]:cu[b + 1]]), ro[cu[b]:cu[b + 1]], f"{case} seq {b}")
+        check_lse(np32(lse[cu[b]:cu[b + 1]]), rl[cu[b]:cu[b + 1]], f"{case} seq {b}",
+                  LSE_ATOL_BF16)
+
+
+@pytest.mark.parametrize("case", PAGED_DECODE, ids=_id)
+def test_random_decode_paged(case):
+    B, H_q, H_kv, T_q, lens, cap, page = case
+    w = inputs.Workload("t", "decode_multi", B=B, H_q=H_q, H_kv=H_kv, d=128, dtype="bf16",
+                        lens=lens, kv_cap=cap, T_q=T_q)
+    banner("random_decode_paged", case)
+    x = inputs.make_decode_paged(w, page, device=DEV, seed=7400 + PAGED_DECODE.index(case))
+    o, lse = gq.decode_paged(x["q"], x["k_pages"], x["v_pages"], x["block_table"], x["kv_lens"],
+                             max_kv_len=max(lens), scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(np32(x["q"]), np32(x["k_pages"]), np32(x["v_pages"]),
+                                 x["block_table"].cpu().numpy(), np.array(lens), page, w.scale)
+    for b in range(B):
+        check_bf16(np32(o[b]), ro[b], f"{case} seq {b}")
+    check_lse(np32(lse), rl, str(case), LSE_ATOL_BF16)
+
+
+@pytest.mark.parametrize("case", PAGED_PREFILL, ids=_id)
+def test_random_prefill_paged(case):
+    H_q, H_kv, q_lens, lens, cap, causal, page = case
+    w = inputs.Workload("t", "prefill_paged", B=len(q_lens), H_q=H_q, H_kv=H_kv, d=128,
+                        dtype="bf16", q_lens=q_lens, lens=lens, kv_cap=cap, causal=causal,
+                        page_size=page)
+    banner("random_prefill_paged", case)
+    x = inputs.make_prefill_paged(w, page, device=DEV, seed=7500 + PAGED_PREFILL.index(case))
+    o, lse = gq.prefill_paged(x["q"], x["k_pages"], x["v_pages"], x["block_table"],
+                              x["cu_seqlens_q"], x["kv_lens"], max_seqlen_q=max(max(q_lens), 1),
+                              max_kv_len=max(max(lens), 1), causal=causal, scale=w.scale,
+                              return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_paged(np32(x["q"]), np32(x["k_pages"]), np32(x["v_pages"]),
+                                  x["block_table"].cpu().numpy(), x["cu_seqlens_q"].cpu().numpy(),
+                                  np.array(lens), page, w.scale, causal=causal)
     cu = x["cu_seqlens_q"].cpu().tolist()
     for b in range(len(q_lens)):
         if cu[b + 1] == cu[b]:
